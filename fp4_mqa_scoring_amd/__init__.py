@@ -1,0 +1,240 @@
+"""MI355X-native FP4 paged-MQA prefill indexer fused with exact TopK.
+
+Thin Python binding of the C ABI in ``include/mqa_fp4_topk.h``: every entry
+point below marshals torch tensors (device memory, streams) into pointers and
+sizes and calls the HIP library ``libmqa_fp4.so``; all arithmetic runs in the
+library's kernels. The library is built in-tree by ``build.build()``; calling
+an entry point without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import synth  # noqa: F401  (seeded input generator)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmqa_fp4.so")
+
+MQA_OK = 0
+ERRORS = {
+    -1: "MQA_ERR_UNSUPPORTED_K", -2: "MQA_ERR_NULL_POINTER", -3: "MQA_ERR_MISALIGNED",
+    -4: "MQA_ERR_BAD_SIZE", -5: "MQA_ERR_DEVICE", -6: "MQA_ERR_CAPTURING", -7: "MQA_ERR_HIP",
+    -8: "MQA_ERR_BAD_FLAGS",
+}
+ROW_BAD_WINDOW, ROW_BAD_PAGE, ROW_UNDERFILL, ROW_SELECTOR = -1, -2, -3, -4
+STATUS_BAD_WINDOW, STATUS_BAD_PAGE, STATUS_UNDERFILL, STATUS_SELECTOR = 1, 2, 4, 8
+FLAG_SPLITS_MASK = 0xFF
+
+
+class MQAError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({_error_string(code)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
+                               "`python -m fp4_mqa_scoring_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+        prefill = [P, P, i64, P, P, i64, P, P, i64, P, P, i32, P, P, P]
+        L.mqa_fp4_topk_prefill.argtypes = prefill + [P]
+        L.mqa_fp4_topk_prefill_ex.argtypes = prefill + [P, u32, P]
+        L.mqa_fp4_dense_topk_prefill.argtypes = [P, P, i64, P, P, i64, P, P, i64, P, P, i32, P, P, P, P, P, P]
+        L.mqa_fp4_dense_logits.argtypes = [P, P, i64, P, P, i64, P, P, i64, P, P, P, P]
+        L.mqa_fp4_logits_topk.argtypes = [P, i64, P, i64, i64, P, P, i32, P, P, P, P, P]
+        L.mqa_fp4_supported_k.argtypes = [P, i32, P]
+        L.mqa_fp4_topk_scratch_bytes.argtypes = [i64, i32, i32]
+        L.mqa_fp4_topk_scratch_bytes.restype = i64
+        L.mqa_fp4_status.argtypes = [P, P]
+        L.mqa_fp4_error_string.argtypes = [i32]
+        L.mqa_fp4_error_string.restype = ctypes.c_char_p
+        L.mqa_fp4_abi_version.argtypes = []
+        for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
+                     "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
+                     "mqa_fp4_status", "mqa_fp4_abi_version"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def _error_string(code: int) -> str:
+    try:
+        return lib().mqa_fp4_error_string(int(code)).decode()
+    except Exception:  # library missing
+        return ""
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(t, name, dtype, ndim=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end):
+    import torch
+    _check(q, "q", torch.uint8, 3)
+    _check(q_scale, "q_scale", torch.uint8, 3)
+    _check(k_pages, "k_pages", torch.uint8, 3)
+    _check(k_scale, "k_scale", torch.uint8, 3)
+    _check(weights, "weights", torch.float32, 2)
+    _check(page_table, "page_table", torch.int32, 1)
+    _check(row_start, "row_start", torch.int32, 1)
+    _check(row_end, "row_end", torch.int32, 1)
+    Q = q.shape[0]
+    if tuple(q.shape[1:]) != (64, 64) or tuple(q_scale.shape) != (Q, 64, 4):
+        raise ValueError("q must be [Q,64,64] and q_scale [Q,64,4]")
+    if tuple(k_pages.shape[1:]) != (64, 64) or tuple(k_scale.shape) != (k_pages.shape[0], 64, 4):
+        raise ValueError("k_pages must be [P,64,64] and k_scale [P,64,4]")
+    if tuple(weights.shape) != (Q, 64) or row_start.shape[0] != Q or row_end.shape[0] != Q:
+        raise ValueError("weights must be [Q,64]; row_start/row_end [Q]")
+    return Q, k_pages.shape[0], page_table.shape[0]
+
+
+def _check_outputs(Q, K, out_raw, out_slot, out_count, out_score):
+    import torch
+    _check(out_raw, "out_raw", torch.int32, 2)
+    _check(out_slot, "out_slot", torch.int32, 2)
+    _check(out_count, "out_count", torch.int32, 1)
+    _check(out_score, "out_score", torch.float32, 2)
+    for t, n in ((out_raw, "out_raw"), (out_slot, "out_slot"), (out_score, "out_score")):
+        if t is not None and tuple(t.shape) != (Q, K):
+            raise ValueError(f"{n} must be [Q, K] = [{Q}, {K}]")
+    if out_count.shape[0] != Q:
+        raise ValueError("out_count must be [Q]")
+
+
+def _rc(code, what):
+    if code != MQA_OK:
+        raise MQAError(code, what)
+
+
+def alloc_outputs(Q: int, K: int, device, with_score: bool = False):
+    """Output buffers (out_raw, out_slot, out_count[, out_score]) on ``device``."""
+    import torch
+    out = [torch.empty((Q, K), dtype=torch.int32, device=device),
+           torch.empty((Q, K), dtype=torch.int32, device=device),
+           torch.empty((Q,), dtype=torch.int32, device=device)]
+    if with_score:
+        out.append(torch.empty((Q, K), dtype=torch.float32, device=device))
+    return tuple(out)
+
+
+def mqa_fp4_topk_prefill(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,
+                         out_raw, out_slot, out_count, stream=None):
+    """Fused FP4 indexer scoring + exact TopK + page mapping (see the C header)."""
+    return mqa_fp4_topk_prefill_ex(q, q_scale, k_pages, k_scale, weights, page_table, row_start,
+                                   row_end, K, out_raw, out_slot, out_count, None, 0, stream)
+
+
+def mqa_fp4_topk_prefill_ex(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,
+                            out_raw, out_slot, out_count, out_score=None, flags=0, stream=None):
+    Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    rc = lib().mqa_fp4_topk_prefill_ex(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), P_phys, _ptr(weights),
+        _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), _ptr(out_raw), _ptr(out_slot),
+        _ptr(out_count), _ptr(out_score), int(flags), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_topk_prefill_ex")
+
+
+def mqa_fp4_dense_topk_prefill(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,
+                               logits, out_raw, out_slot, out_count, out_score=None, stream=None):
+    """Dense comparator: fp32 logits [Q, S] (caller-owned), then exact TopK."""
+    import torch
+    Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    _check(logits, "logits", torch.float32, 2)
+    if tuple(logits.shape) != (Q, 64 * P_log):
+        raise ValueError("logits must be [Q, 64 * P_log]")
+    rc = lib().mqa_fp4_dense_topk_prefill(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), P_phys, _ptr(weights),
+        _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), _ptr(logits), _ptr(out_raw),
+        _ptr(out_slot), _ptr(out_count), _ptr(out_score), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_dense_topk_prefill")
+
+
+def mqa_fp4_dense_logits(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, logits,
+                         stream=None):
+    import torch
+    Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
+    _check(logits, "logits", torch.float32, 2)
+    if tuple(logits.shape) != (Q, 64 * P_log):
+        raise ValueError("logits must be [Q, 64 * P_log]")
+    rc = lib().mqa_fp4_dense_logits(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), P_phys, _ptr(weights),
+        _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), _ptr(logits), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_dense_logits")
+
+
+def mqa_fp4_logits_topk(logits, page_table, num_phys_pages, row_start, row_end, K, out_raw, out_slot,
+                        out_count, out_score=None, stream=None):
+    """Exact TopK over caller-provided fp32 logits [Q, 64 * P_log]."""
+    import torch
+    _check(logits, "logits", torch.float32, 2)
+    _check(page_table, "page_table", torch.int32, 1)
+    _check(row_start, "row_start", torch.int32, 1)
+    _check(row_end, "row_end", torch.int32, 1)
+    Q, P_log = logits.shape[0], page_table.shape[0]
+    if logits.shape[1] != 64 * P_log:
+        raise ValueError("logits must be [Q, 64 * P_log]")
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    rc = lib().mqa_fp4_logits_topk(
+        _ptr(logits), Q, _ptr(page_table), P_log, int(num_phys_pages), _ptr(row_start), _ptr(row_end),
+        int(K), _ptr(out_raw), _ptr(out_slot), _ptr(out_count), _ptr(out_score),
+        _stream(stream, logits.device))
+    _rc(rc, "mqa_fp4_logits_topk")
+
+
+def mqa_fp4_supported_k():
+    buf = (ctypes.c_int32 * 8)()
+    n = ctypes.c_int32(0)
+    _rc(lib().mqa_fp4_supported_k(buf, 8, ctypes.byref(n)), "mqa_fp4_supported_k")
+    return [int(buf[i]) for i in range(n.value)]
+
+
+def mqa_fp4_topk_scratch_bytes(num_rows: int, K: int, device: int = 0) -> int:
+    r = int(lib().mqa_fp4_topk_scratch_bytes(int(num_rows), int(K), int(device)))
+    if r < 0:
+        raise MQAError(r, "mqa_fp4_topk_scratch_bytes")
+    return r
+
+
+def mqa_fp4_status(stream=None, device=None) -> int:
+    """Synchronises the stream, returns and clears the sticky status bits."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    st = ctypes.c_int32(0)
+    _rc(lib().mqa_fp4_status(_stream(stream, dev), ctypes.byref(st)), "mqa_fp4_status")
+    return int(st.value)
+
+
+def mqa_fp4_abi_version() -> int:
+    return int(lib().mqa_fp4_abi_version())

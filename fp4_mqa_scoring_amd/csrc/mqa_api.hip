@@ -1,0 +1,400 @@
+// Host side of the C ABI declared in include/mqa_fp4_topk.h.
+//
+// Fail-closed host checks (PR 5309 "[FlyDSL] Add FP4 LiteTopK prefill
+// operator", Implementation: explicit supported-K contract, fail closed,
+// preserve caller device/stream ownership, 64-bit addressing), graph-capture
+// rejection (PR 5282, Scope), launch planning and stream-ordered scratch.
+#include "mqa_fp4_topk.h"
+#include "mqa_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+namespace {
+
+using mqa::PathArgs;
+
+constexpr int kMaxDevices = 64;
+constexpr int kRowsPerCta = 8;       // must match the kernels' row tile
+constexpr int kMaxAutoSplits = 64;
+
+struct DeviceInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int cus = 0;
+  bool pool_ready = false;
+};
+
+std::mutex g_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+// Probes (once) whether `dev` is a gfx950 and how many CUs it has.
+int32_t device_info(int dev, DeviceInfo* out) {
+  if (dev < 0 || dev >= kMaxDevices) return MQA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MQA_ERR_HIP;
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.probed = true;
+  }
+  if (!d.pool_ready && d.gfx950) {
+    // keep freed scratch in the device's default pool instead of returning it
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+      uint64_t thr = ~0ull;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+    }
+    (void)hipGetLastError();
+    d.pool_ready = true;
+  }
+  *out = d;
+  return d.gfx950 ? MQA_OK : MQA_ERR_DEVICE;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int saved = -1;
+  bool changed = false;
+  int32_t enter(int dev) {
+    if (hipGetDevice(&saved) != hipSuccess) return MQA_ERR_HIP;
+    if (saved != dev) {
+      if (hipSetDevice(dev) != hipSuccess) return MQA_ERR_HIP;
+      changed = true;
+    }
+    return MQA_OK;
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(saved);
+  }
+};
+
+int32_t stream_device(hipStream_t st, int* dev) {
+  if (st == nullptr) return hipGetDevice(dev) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+  return hipStreamGetDevice(st, dev) == hipSuccess ? MQA_OK : MQA_ERR_DEVICE;
+}
+
+// A non-null pointer must be device (or managed) memory of device `dev`.
+int32_t check_ptr_device(const void* p, int dev) {
+  if (p == nullptr) return MQA_OK;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return MQA_ERR_DEVICE;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return MQA_ERR_DEVICE;
+  if (attr.device != dev) return MQA_ERR_DEVICE;
+  return MQA_OK;
+}
+
+struct PtrSpec {
+  const void* p;
+  bool required;
+  uintptr_t align;
+};
+
+// Host-only pointer checks (no HIP call): presence and alignment.
+int32_t check_ptrs_host(const PtrSpec* specs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (specs[i].required && specs[i].p == nullptr) return MQA_ERR_NULL_POINTER;
+  for (int i = 0; i < n; ++i)
+    if (specs[i].p && reinterpret_cast<uintptr_t>(specs[i].p) % specs[i].align) return MQA_ERR_MISALIGNED;
+  return MQA_OK;
+}
+
+int32_t check_ptrs_device(const PtrSpec* specs, int n, int dev) {
+  for (int i = 0; i < n; ++i) {
+    const int32_t rc = check_ptr_device(specs[i].p, dev);
+    if (rc != MQA_OK) return rc;
+  }
+  return MQA_OK;
+}
+
+int32_t check_sizes(int64_t Q, int64_t P_phys, int64_t P_log) {
+  if (Q < 0 || P_phys < 0 || P_log < 0) return MQA_ERR_BAD_SIZE;
+  if (Q > 0x7FFFFFFFll) return MQA_ERR_BAD_SIZE;                 // grid size, row index
+  if (P_log > (0x7FFFFFFFll - 512) / 64) return MQA_ERR_BAD_SIZE; // positions in int32
+  if (P_phys > 0x7FFFFFFFll / 64) return MQA_ERR_BAD_SIZE;        // slots in int32
+  return MQA_OK;
+}
+
+int32_t check_capture(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return MQA_ERR_HIP;
+  }
+  return cs == hipStreamCaptureStatusNone ? MQA_OK : MQA_ERR_CAPTURING;
+}
+
+int32_t auto_splits(int64_t Q, int cus) {
+  const int64_t tiles = (Q + kRowsPerCta - 1) / kRowsPerCta;
+  if (tiles <= 0) return 1;
+  int64_t s = (2 * static_cast<int64_t>(cus) + tiles - 1) / tiles;
+  if (s < 1) s = 1;
+  if (s > kMaxAutoSplits) s = kMaxAutoSplits;
+  return static_cast<int32_t>(s);
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct FusedScratch {
+  size_t state_off, keys_off, count_off, total;
+};
+
+FusedScratch fused_scratch_layout(int64_t Q, int32_t K, int32_t splits) {
+  FusedScratch s;
+  s.state_off = 0;
+  s.keys_off = align_up(static_cast<size_t>(Q) * sizeof(int32_t));
+  s.count_off = s.keys_off + align_up(static_cast<size_t>(Q) * splits * K * sizeof(uint64_t));
+  s.total = s.count_off + align_up(static_cast<size_t>(Q) * splits * sizeof(int32_t));
+  return s;
+}
+
+// Common entry checks; on success the guard holds the tensors' device.
+// Order: host-only checks first (testable without a GPU), then device checks.
+int32_t enter(hipStream_t st, const PtrSpec* specs, int nspecs, DeviceGuard& guard, DeviceInfo* info) {
+  int32_t rc = check_ptrs_host(specs, nspecs);
+  if (rc != MQA_OK) return rc;
+  int dev = -1;
+  rc = stream_device(st, &dev);
+  if (rc != MQA_OK) return rc;
+  rc = check_capture(st);
+  if (rc != MQA_OK) return rc;
+  rc = device_info(dev, info);
+  if (rc != MQA_OK) return rc;
+  rc = check_ptrs_device(specs, nspecs, dev);
+  if (rc != MQA_OK) return rc;
+  return guard.enter(dev);
+}
+
+// Stream-ordered scratch for one call.
+struct Scratch {
+  void* p = nullptr;
+  hipStream_t st = nullptr;
+  int32_t alloc(size_t bytes, hipStream_t stream) {
+    st = stream;
+    if (bytes == 0) return MQA_OK;
+    if (hipMallocAsync(&p, bytes, stream) != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+      return MQA_ERR_HIP;
+    }
+    return MQA_OK;
+  }
+  ~Scratch() {
+    if (p) (void)hipFreeAsync(p, st);
+  }
+};
+
+int32_t hip_rc(hipError_t e) {
+  if (e == hipSuccess) return MQA_OK;
+  (void)hipGetLastError();
+  return MQA_ERR_HIP;
+}
+
+int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
+  if (p.K != 512 && p.K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (flags & ~static_cast<uint32_t>(MQA_FLAG_SPLITS_MASK)) return MQA_ERR_BAD_FLAGS;
+  int32_t rc = check_sizes(p.Q, p.P_phys, p.P_log);
+  if (rc != MQA_OK) return rc;
+  const bool rows = p.Q > 0;
+  const PtrSpec specs[] = {
+      {p.q, rows, 16},          {p.q_scale, rows, 4},   {p.k_pages, p.P_phys > 0, 16},
+      {p.k_scale, p.P_phys > 0, 16}, {p.weights, rows, 4}, {p.page_table, p.P_log > 0, 4},
+      {p.row_start, rows, 4},   {p.row_end, rows, 4},   {p.out_raw, rows, 4},
+      {p.out_slot, rows, 4},    {p.out_count, rows, 4}, {p.out_score, false, 4},
+  };
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  if (rc != MQA_OK) return rc;
+  if (!rows) return MQA_OK;
+  const int32_t splits = (flags & MQA_FLAG_SPLITS_MASK) ? static_cast<int32_t>(flags & MQA_FLAG_SPLITS_MASK)
+                                                        : auto_splits(p.Q, info.cus);
+  const FusedScratch lay = fused_scratch_layout(p.Q, p.K, splits);
+  Scratch scratch;
+  rc = scratch.alloc(lay.total, st);
+  if (rc != MQA_OK) return rc;
+  char* base = static_cast<char*>(scratch.p);
+  int32_t* row_state = reinterpret_cast<int32_t*>(base + lay.state_off);
+  uint64_t* keys = reinterpret_cast<uint64_t*>(base + lay.keys_off);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + lay.count_off);
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_fused(p, row_state, splits, keys, counts, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_merge(p, row_state, splits, keys, counts, st));
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mqa_fp4_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                             const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                             const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                             const int32_t* row_start, const int32_t* row_end, int32_t K, int32_t* out_raw,
+                             int32_t* out_slot, int32_t* out_count, void* stream) {
+  return mqa_fp4_topk_prefill_ex(q, q_scale, num_rows, k_pages, k_scale, num_phys_pages, weights, page_table,
+                                 num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count,
+                                 nullptr, 0u, stream);
+}
+
+int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                                const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                                const int32_t* row_start, const int32_t* row_end, int32_t K, int32_t* out_raw,
+                                int32_t* out_slot, int32_t* out_count, float* out_score, uint32_t flags,
+                                void* stream) {
+  const PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  page_table,
+                   num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  return run_fused(p, flags, static_cast<hipStream_t>(stream));
+}
+
+int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                   const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                                   const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                                   const int32_t* row_start, const int32_t* row_end, int32_t K, float* logits,
+                                   int32_t* out_raw, int32_t* out_slot, int32_t* out_count, float* out_score,
+                                   void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  int32_t rc = check_sizes(num_rows, num_phys_pages, num_logical_pages);
+  if (rc != MQA_OK) return rc;
+  const bool rows = num_rows > 0;
+  const PtrSpec specs[] = {
+      {q, rows, 16},          {q_scale, rows, 4},   {k_pages, num_phys_pages > 0, 16},
+      {k_scale, num_phys_pages > 0, 16}, {weights, rows, 4}, {page_table, num_logical_pages > 0, 4},
+      {row_start, rows, 4},   {row_end, rows, 4},   {logits, rows && num_logical_pages > 0, 4},
+      {out_raw, rows, 4},     {out_slot, rows, 4},  {out_count, rows, 4}, {out_score, false, 4},
+  };
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  if (rc != MQA_OK) return rc;
+  if (!rows) return MQA_OK;
+  const PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  page_table,
+                   num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  Scratch scratch;
+  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  if (rc != MQA_OK) return rc;
+  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
+  return rc;
+}
+
+int32_t mqa_fp4_dense_logits(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows, const uint8_t* k_pages,
+                             const uint8_t* k_scale, int64_t num_phys_pages, const float* weights,
+                             const int32_t* page_table, int64_t num_logical_pages, const int32_t* row_start,
+                             const int32_t* row_end, float* logits, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t rc = check_sizes(num_rows, num_phys_pages, num_logical_pages);
+  if (rc != MQA_OK) return rc;
+  const bool rows = num_rows > 0;
+  const PtrSpec specs[] = {
+      {q, rows, 16},          {q_scale, rows, 4},   {k_pages, num_phys_pages > 0, 16},
+      {k_scale, num_phys_pages > 0, 16}, {weights, rows, 4}, {page_table, num_logical_pages > 0, 4},
+      {row_start, rows, 4},   {row_end, rows, 4},   {logits, rows && num_logical_pages > 0, 4},
+  };
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  if (rc != MQA_OK) return rc;
+  if (!rows) return MQA_OK;
+  const PathArgs p{q,       q_scale, num_rows, k_pages, k_scale, num_phys_pages, weights, page_table,
+                   num_logical_pages, row_start, row_end, 0, nullptr, nullptr, nullptr, nullptr};
+  Scratch scratch;
+  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  if (rc != MQA_OK) return rc;
+  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  rc = hip_rc(mqa::launch_row_prep(p, 1, row_state, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
+  return rc;
+}
+
+int32_t mqa_fp4_logits_topk(const float* logits, int64_t num_rows, const int32_t* page_table,
+                            int64_t num_logical_pages, int64_t num_phys_pages, const int32_t* row_start,
+                            const int32_t* row_end, int32_t K, int32_t* out_raw, int32_t* out_slot,
+                            int32_t* out_count, float* out_score, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  int32_t rc = check_sizes(num_rows, num_phys_pages, num_logical_pages);
+  if (rc != MQA_OK) return rc;
+  const bool rows = num_rows > 0;
+  const PtrSpec specs[] = {
+      {logits, rows && num_logical_pages > 0, 4}, {page_table, num_logical_pages > 0, 4},
+      {row_start, rows, 4}, {row_end, rows, 4}, {out_raw, rows, 4}, {out_slot, rows, 4},
+      {out_count, rows, 4}, {out_score, false, 4},
+  };
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  if (rc != MQA_OK) return rc;
+  if (!rows) return MQA_OK;
+  const PathArgs p{nullptr, nullptr, num_rows, nullptr, nullptr, num_phys_pages, nullptr, page_table,
+                   num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  Scratch scratch;
+  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  if (rc != MQA_OK) return rc;
+  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
+  return rc;
+}
+
+int32_t mqa_fp4_supported_k(int32_t* ks, int32_t capacity, int32_t* n) {
+  static const int32_t kSupported[2] = {512, 1024};
+  if (n == nullptr) return MQA_ERR_NULL_POINTER;
+  *n = 2;
+  if (ks != nullptr)
+    for (int32_t i = 0; i < capacity && i < 2; ++i) ks[i] = kSupported[i];
+  return MQA_OK;
+}
+
+int64_t mqa_fp4_topk_scratch_bytes(int64_t num_rows, int32_t K, int32_t device) {
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (num_rows < 0 || num_rows > 0x7FFFFFFFll) return MQA_ERR_BAD_SIZE;
+  DeviceInfo info;
+  const int32_t rc = device_info(device, &info);
+  if (rc != MQA_OK) return rc;
+  if (num_rows == 0) return 0;
+  return static_cast<int64_t>(fused_scratch_layout(num_rows, K, auto_splits(num_rows, info.cus)).total);
+}
+
+int32_t mqa_fp4_status(void* stream, int32_t* status) {
+  if (status == nullptr) return MQA_ERR_NULL_POINTER;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  int32_t rc = stream_device(st, &dev);
+  if (rc != MQA_OK) return rc;
+  DeviceGuard guard;
+  rc = guard.enter(dev);
+  if (rc != MQA_OK) return rc;
+  return hip_rc(mqa::status_take(st, status));
+}
+
+const char* mqa_fp4_error_string(int32_t code) {
+  switch (code) {
+    case MQA_OK: return "ok";
+    case MQA_ERR_UNSUPPORTED_K: return "unsupported K (supported: 512, 1024)";
+    case MQA_ERR_NULL_POINTER: return "required pointer is NULL";
+    case MQA_ERR_MISALIGNED: return "pointer misaligned";
+    case MQA_ERR_BAD_SIZE: return "size out of range";
+    case MQA_ERR_DEVICE: return "pointer/stream/device mismatch or device is not gfx950";
+    case MQA_ERR_CAPTURING: return "stream is capturing a graph (not supported)";
+    case MQA_ERR_HIP: return "HIP runtime error";
+    case MQA_ERR_BAD_FLAGS: return "unknown flag bits";
+    default: return "unknown error";
+  }
+}
+
+int32_t mqa_fp4_abi_version(void) { return MQA_FP4_ABI_VERSION; }
+
+}  // extern "C"

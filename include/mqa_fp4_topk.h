@@ -1,0 +1,181 @@
+/*
+ * mqa_fp4_topk.h -- C ABI of the MI355X (gfx950) FP4 paged-MQA prefill indexer
+ * fused with exact TopK.
+ *
+ * What the operator computes
+ * --------------------------
+ * Sources: "[FlyDSL] Add FP4 LiteTopK prefill operator" (ROCm/aiter PR 5309),
+ * Summary and Implementation; "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
+ * (ROCm/aiter PR 5282), Changes and Scope.
+ *
+ * For every query row q and every logical C4 position s of the row's window
+ * [row_start[q], row_end[q]) the DeepSeek-V4 indexer score is
+ *
+ *     score[q, s] = sum_{h<64} weights[q, h] * ReLU(dot_h(q, s))
+ *     dot_h(q, s) = sum_{b<4} 2^(qs[q,h,b]-127) * 2^(ks[s,b]-127)
+ *                   * sum_{j<32} e2m1(q[q,h,32b+j]) * e2m1(k[s,32b+j])
+ *
+ * computed in fp32 (ReLU(x) = x if x > 0 else +0). Each row returns the K
+ * positions first in the total order "score descending, then logical index
+ * ascending; NaN below every number; +0 above -0" (PR 5282, Changes), written
+ * in ascending position order, together with their physical cache slots
+ * page_table[s / 64] * 64 + s % 64 and a valid count. A row whose window
+ * length is <= K returns every position of the window in order, padded with
+ * -1 (PR 5282, Changes: short-row contract). The [Q, S] score matrix is never
+ * materialised by mqa_fp4_topk_prefill; its scratch does not depend on S.
+ *
+ * Data layout (all tensors C-contiguous, all pointers DEVICE pointers on one
+ * gfx950 device, owned by the caller; the library never frees or keeps them):
+ *   q          uint8  [Q, 64, 64]        E2M1 codes, element 2j = low nibble of byte j
+ *   q_scale    uint8  [Q, 64, 4]         UE8M0 byte per 32 elements along D=128
+ *   k_pages    uint8  [P_phys, 64, 64]   paged C4 key cache, page size 64
+ *   k_scale    uint8  [P_phys, 64, 4]
+ *   weights    float  [Q, 64]
+ *   page_table int32  [P_log]            logical page -> physical page; S = 64 * P_log
+ *   row_start, row_end int32 [Q]         window [start, end) in logical C4 positions
+ *   out_raw, out_slot  int32 [Q, K]      written in place (PR 38101 of sglang, Changes:
+ *                                        "write final physical C4 slots and optional
+ *                                        raw indices in place")
+ *   out_count  int32  [Q]                min(len, K), or a negative per-row code
+ *   out_score  float  [Q, K] (optional)  fp32 score of each selected position;
+ *                                        NaN for padding and for short rows
+ * q, k_pages and k_scale must be 16-byte aligned, the others 4-byte aligned.
+ *
+ * Errors (fail closed, PR 5309 Implementation)
+ * --------------------------------------------
+ * A negative return value is a host-detected error: nothing was launched and no
+ * output was written. A row that the device finds invalid gets out_raw and
+ * out_slot all -1 and a negative out_count (MQA_ROW_*), and sets a sticky bit
+ * in the per-device status word read by mqa_fp4_status().
+ *
+ * Streams and devices (PR 5309 Implementation: preserve caller device/stream
+ * ownership, 64-bit addressing). Work is enqueued on `stream` (a hipStream_t;
+ * NULL = the legacy default stream of the current device), which must belong to
+ * the device the tensors live on; the caller's current device is restored
+ * before returning. The success path never synchronises. Graph capture is
+ * rejected (PR 5282, Scope: graph capture is rejected explicitly in this first
+ * version). Calls on the same stream are ordered; calls on different streams
+ * use separate stream-ordered scratch and may run concurrently.
+ */
+#ifndef MQA_FP4_TOPK_H
+#define MQA_FP4_TOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------- */
+#define MQA_OK 0
+#define MQA_ERR_UNSUPPORTED_K (-1)   /* K not in {512, 1024} (PR 5309: explicit supported-K contract) */
+#define MQA_ERR_NULL_POINTER (-2)    /* a required pointer is NULL while its tensor is non-empty */
+#define MQA_ERR_MISALIGNED (-3)      /* a pointer breaks the alignment stated above */
+#define MQA_ERR_BAD_SIZE (-4)        /* negative size, or 64*P_log / 64*P_phys / Q*K beyond int32 */
+#define MQA_ERR_DEVICE (-5)          /* not device memory, tensors on different devices, stream on
+                                        another device, or the device is not gfx950 */
+#define MQA_ERR_CAPTURING (-6)       /* the stream is capturing a graph */
+#define MQA_ERR_HIP (-7)             /* a HIP runtime call failed (allocation, launch) */
+#define MQA_ERR_BAD_FLAGS (-8)       /* unknown bits in flags */
+
+/* ---- per-row codes in out_count -------------------------------------------- */
+#define MQA_ROW_BAD_WINDOW (-1)      /* start < 0, end < start or end > 64 * P_log */
+#define MQA_ROW_BAD_PAGE (-2)        /* a page touched by the window maps outside [0, P_phys) */
+#define MQA_ROW_UNDERFILL (-3)       /* fewer than K candidates survived and the fallback failed */
+#define MQA_ROW_SELECTOR (-4)        /* internal selection invariant violated */
+
+/* ---- sticky status bits ---------------------------------------------------- */
+#define MQA_STATUS_BAD_WINDOW 1
+#define MQA_STATUS_BAD_PAGE 2
+#define MQA_STATUS_UNDERFILL 4
+#define MQA_STATUS_SELECTOR 8
+
+/* ---- flags of the _ex entry point -------------------------------------------- */
+#define MQA_FLAG_SPLITS_MASK 0xFFu   /* context splits per row tile, 0 = automatic (1..255) */
+
+/*
+ * Fused FP4 scoring + exact TopK + page mapping (the hot path).
+ *   num_rows          Q >= 0
+ *   num_phys_pages    P_phys >= 0, 64 * P_phys <= INT32_MAX
+ *   num_logical_pages P_log >= 0, 64 * P_log <= INT32_MAX
+ *   K                 512 or 1024
+ * Returns MQA_OK or a negative MQA_ERR_*.
+ */
+int32_t mqa_fp4_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                             const uint8_t* k_pages, const uint8_t* k_scale,
+                             int64_t num_phys_pages, const float* weights,
+                             const int32_t* page_table, int64_t num_logical_pages,
+                             const int32_t* row_start, const int32_t* row_end, int32_t K,
+                             int32_t* out_raw, int32_t* out_slot, int32_t* out_count,
+                             void* stream);
+
+/* As mqa_fp4_topk_prefill, plus an optional fp32 score output (NULL = none)
+ * and flags (MQA_FLAG_*). Outputs do not depend on the splits chosen. */
+int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                const uint8_t* k_pages, const uint8_t* k_scale,
+                                int64_t num_phys_pages, const float* weights,
+                                const int32_t* page_table, int64_t num_logical_pages,
+                                const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                int32_t* out_raw, int32_t* out_slot, int32_t* out_count,
+                                float* out_score, uint32_t flags, void* stream);
+
+/*
+ * Dense comparator (the legacy full-logits path the pages measure against:
+ * PR 5282 Motivation, "materializes an FP32 [query_rows, c4_context] score
+ * matrix before TopK"). Writes the fp32 score of every position inside each
+ * long row's window (length > K) into logits[q * 64 * P_log + s] (caller-owned
+ * [Q, S] buffer; entries outside those windows are left untouched), then selects
+ * exactly as mqa_fp4_topk_prefill. Scores are bit-identical to the fused path.
+ */
+int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                   const uint8_t* k_pages, const uint8_t* k_scale,
+                                   int64_t num_phys_pages, const float* weights,
+                                   const int32_t* page_table, int64_t num_logical_pages,
+                                   const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                   float* logits, int32_t* out_raw, int32_t* out_slot,
+                                   int32_t* out_count, float* out_score, void* stream);
+
+/* The dense path's scorer alone: logits as above, for every row with a valid
+ * window and valid pages (no length condition). */
+int32_t mqa_fp4_dense_logits(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                             const uint8_t* k_pages, const uint8_t* k_scale,
+                             int64_t num_phys_pages, const float* weights,
+                             const int32_t* page_table, int64_t num_logical_pages,
+                             const int32_t* row_start, const int32_t* row_end, float* logits,
+                             void* stream);
+
+/* The dense path's selector alone: exact TopK over caller-provided fp32 logits
+ * [Q, 64 * P_log] under the same total order, windows, short-row rule, page
+ * validation and page mapping. */
+int32_t mqa_fp4_logits_topk(const float* logits, int64_t num_rows, const int32_t* page_table,
+                            int64_t num_logical_pages, int64_t num_phys_pages,
+                            const int32_t* row_start, const int32_t* row_end, int32_t K,
+                            int32_t* out_raw, int32_t* out_slot, int32_t* out_count,
+                            float* out_score, void* stream);
+
+/* Capability probe (sglang PR 38101, Dependency: probe by exact symbol).
+ * Writes up to `capacity` supported K values into ks and their number into *n. */
+int32_t mqa_fp4_supported_k(int32_t* ks, int32_t capacity, int32_t* n);
+
+/* Bytes of stream-ordered device scratch mqa_fp4_topk_prefill allocates for
+ * num_rows rows on `device` (independent of the context length); negative on
+ * error. */
+int64_t mqa_fp4_topk_scratch_bytes(int64_t num_rows, int32_t K, int32_t device);
+
+/* Synchronises `stream`, then returns in *status the OR of the sticky status
+ * bits set by calls on the stream's device since the last read, and clears
+ * them. */
+int32_t mqa_fp4_status(void* stream, int32_t* status);
+
+/* Static description of a return code. */
+const char* mqa_fp4_error_string(int32_t code);
+
+/* ABI version of this header (incremented on incompatible change). */
+int32_t mqa_fp4_abi_version(void);
+#define MQA_FP4_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQA_FP4_TOPK_H */

@@ -1,0 +1,80 @@
+"""CPU checks of the C ABI: the HIP library loads, exports every symbol the
+public header declares, and rejects bad arguments on the host before any HIP
+call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_fp4_topk.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mqa_fp4_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp4_mqa_scoring_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from fp4_mqa_scoring_amd import build
+        build.build()
+    return m.lib()
+
+
+def test_header_declares_the_operator_api():
+    syms = declared_symbols()
+    for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
+                 "mqa_fp4_logits_topk", "mqa_fp4_supported_k", "mqa_fp4_topk_scratch_bytes",
+                 "mqa_fp4_status"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_capability_probe_and_version(lib):
+    import fp4_mqa_scoring_amd as m
+    assert m.mqa_fp4_supported_k() == [512, 1024]
+    assert m.mqa_fp4_abi_version() == 1
+    assert b"unsupported K" in lib.mqa_fp4_error_string(-1)
+
+
+def _call_prefill(lib, K=512, Q=4, P_phys=2, P_log=2, flags=0, ptr=0x1000, **over):
+    args = dict(q=ptr, q_scale=ptr, k_pages=ptr, k_scale=ptr, weights=ptr, page_table=ptr,
+                row_start=ptr, row_end=ptr, out_raw=ptr, out_slot=ptr, out_count=ptr, out_score=None)
+    args.update(over)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.mqa_fp4_topk_prefill_ex(v(args["q"]), v(args["q_scale"]), Q, v(args["k_pages"]),
+                                       v(args["k_scale"]), P_phys, v(args["weights"]),
+                                       v(args["page_table"]), P_log, v(args["row_start"]),
+                                       v(args["row_end"]), K, v(args["out_raw"]), v(args["out_slot"]),
+                                       v(args["out_count"]), v(args["out_score"]), flags, None)
+
+
+@pytest.mark.parametrize("K", [0, 1, 256, 511, 513, 768, 2048, -512])
+def test_unsupported_k_rejected_before_any_device_work(lib, K):
+    assert _call_prefill(lib, K=K) == -1
+
+
+def test_bad_flags_sizes_nulls_alignment_rejected_on_host(lib):
+    assert _call_prefill(lib, flags=0x100) == -8
+    assert _call_prefill(lib, Q=-1) == -4
+    assert _call_prefill(lib, P_log=(1 << 31) // 64) == -4
+    assert _call_prefill(lib, P_phys=(1 << 31) // 64 + 1) == -4
+    assert _call_prefill(lib, q=None) == -2
+    assert _call_prefill(lib, out_count=None) == -2
+    assert _call_prefill(lib, k_pages=0x1008) == -3          # needs 16-byte alignment
+    assert _call_prefill(lib, row_end=0x1002) == -3
+
+
+def test_dense_and_logits_entry_points_check_k_on_host(lib):
+    P = ctypes.c_void_p
+    p = P(0x1000)
+    assert lib.mqa_fp4_dense_topk_prefill(p, p, 1, p, p, 1, p, p, 1, p, p, 7, p, p, p, p, None, None) == -1
+    assert lib.mqa_fp4_logits_topk(p, 1, p, 1, 1, p, p, 100, p, p, p, None, None) == -1

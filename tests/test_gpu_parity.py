@@ -1,0 +1,338 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar (stated per check below): physical slots, counts, short-row padding and
+per-head dot products bit-exact; fp32 scores within 1e-5 of the oracle's
+float64 score relative to the row's magnitude; selected sets equal up to swaps
+that the tolerance allows (oracle/check.py), with exact ties broken by index.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.check import check_long_row, check_short_row, expected_slots
+from fp4_mqa_scoring_amd import synth
+import fp4_mqa_scoring_amd as mqa
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def _need_gpu():
+    if not gu.has_gpu():
+        pytest.skip("no GPU")
+
+
+def check_rows(inp, rows, raw, slot, cnt, score=None, where=""):
+    """Checks the given rows of a GPU result against the oracle."""
+    K = inp.K
+    for r in rows:
+        r = int(r)
+        tag = f"{where} row {r}"
+        v = oracle.validate_row(inp, r)
+        st, en = int(inp.row_start[r]), int(inp.row_end[r])
+        if v < 0:
+            assert cnt[r] == v, f"{tag}: count {cnt[r]} != code {v}"
+            assert np.all(raw[r] == -1) and np.all(slot[r] == -1), tag
+            continue
+        if en - st <= K:
+            check_short_row(st, en, K, raw[r], slot[r], int(cnt[r]), inp.page_table, where=tag)
+            continue
+        sigma, mag = oracle.row_scores(inp, r)
+        sel = None
+        if not np.all(np.isfinite(sigma)):
+            sel = oracle.select_topk(sigma, st, K)[1]
+        check_long_row(sigma, mag, st, K, raw[r], slot[r], int(cnt[r]), inp.page_table, tol=TOL,
+                       oracle_sel=sel, where=tag)
+        if score is not None and np.all(np.isfinite(sigma)):
+            ref = sigma[raw[r] - st]
+            bound = TOL * max(np.abs(sigma).max(), mag.max())
+            err = np.abs(score[r].astype(np.float64) - ref)
+            assert np.all(err <= bound), f"{tag}: score error {err.max()} > {bound}"
+
+
+# --- per-head dot products: bit-exact through the public API --------------------------
+
+def test_per_head_dots_bit_exact_via_one_hot_weights():
+    """Dense logits with weights e_h give ReLU(d_h) exactly; negating the query
+    (XOR 0x88 flips both nibble signs) gives ReLU(-d_h). Together they give d_h,
+    which must equal the oracle's exact dot product bit for bit."""
+    _need_gpu()
+    Q, S = 16, 640
+    st = np.array([0, 5, 64, 100, 0, 3, 200, 1, 0, 0, 7, 9, 300, 11, 0, 2], np.int32)
+    en = np.minimum(st + 600, S).astype(np.int32)
+    inp = synth.make_inputs(Q, S, 512, 4242, row_start=st, row_end=en, P_phys=13)
+    heads = [0, 1, 5, 17, 31, 32, 33, 47, 62, 63]
+    for h in heads:
+        w = np.zeros((Q, 64), np.float32)
+        w[:, h] = 1.0
+        inp.weights = w
+        pos = gu.dense_logits(gu.to_device(inp))
+        neg_inp = synth.Inputs(**{**inp.__dict__, "q": inp.q ^ np.uint8(0x88)})
+        neg = gu.dense_logits(gu.to_device(neg_inp))
+        for r in range(Q):
+            for s in range(int(st[r]), int(en[r]), 37):
+                page = int(inp.page_table[s // 64])
+                d = oracle.head_dot(inp.q[r, h], inp.q_scale[r, h], inp.k_pages[page, s % 64],
+                                    inp.k_scale[page, s % 64])
+                got = float(np.float64(pos[r, s]) - np.float64(neg[r, s]))
+                assert got == d, f"head {h} row {r} pos {s}: {got} != {d}"
+                assert pos[r, s] == max(d, 0.0) and neg[r, s] == max(-d, 0.0)
+
+
+# --- the tiny workload: every row --------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny():
+    inp = synth.make_config(1)
+    return inp, gu.to_device(inp)
+
+
+def test_tiny_fused_matches_oracle_all_rows(tiny):
+    _need_gpu()
+    inp, dev = tiny
+    raw, slot, cnt, score = gu.run_fused(dev, inp.K)
+    check_rows(inp, range(inp.Q), raw, slot, cnt, score, where="tiny fused")
+
+
+def test_tiny_dense_matches_oracle_and_fused_bit_for_bit(tiny):
+    _need_gpu()
+    inp, dev = tiny
+    f = gu.run_fused(dev, inp.K)
+    raw, slot, cnt, score, _ = gu.run_dense(dev, inp.K)
+    check_rows(inp, range(inp.Q), raw, slot, cnt, score, where="tiny dense")
+    assert np.array_equal(f[0], raw) and np.array_equal(f[1], slot) and np.array_equal(f[2], cnt)
+    assert np.array_equal(f[3].view(np.uint32), score.view(np.uint32))
+
+
+def test_dense_logits_match_oracle_scores(tiny):
+    _need_gpu()
+    inp, dev = tiny
+    lg = gu.dense_logits(dev)
+    for r in range(inp.Q):
+        st, en = int(inp.row_start[r]), int(inp.row_end[r])
+        if en <= st:
+            continue
+        sigma, mag = oracle.row_scores(inp, r)
+        bound = TOL * max(np.abs(sigma).max(), mag.max())
+        assert np.all(np.abs(lg[r, st:en].astype(np.float64) - sigma) <= bound), r
+
+
+# --- invariances ------------------------------------------------------------------------------
+
+def medium_inputs(seed=777, Q=20, S=2560, K=512):
+    rng = np.random.default_rng(seed)
+    st = rng.integers(0, 700, Q).astype(np.int32)
+    en = np.minimum(st + rng.integers(K + 1, S, Q), S).astype(np.int32)
+    st[3], en[3] = 0, S                       # full window
+    st[4], en[4] = 10, 10 + K                 # exactly K: short
+    st[5], en[5] = 99, 99 + K + 1             # K + 1: long
+    return synth.make_inputs(Q, S, K, seed, row_start=st, row_end=en, P_phys=S // 64 + 3)
+
+
+@pytest.mark.parametrize("K", [512, 1024])
+def test_splits_do_not_change_outputs(K):
+    _need_gpu()
+    inp = medium_inputs(K=K, S=4096 if K == 1024 else 2560)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K)
+    check_rows(inp, range(inp.Q), base[0], base[1], base[2], base[3], where=f"medium K={K}")
+    for splits in (1, 2, 3, 4, 8, 17):
+        got = gu.run_fused(dev, K, flags=splits)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"splits={splits}"
+
+
+def test_non_default_stream_gives_same_outputs():
+    _need_gpu()
+    import torch
+    inp = medium_inputs(seed=31)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, inp.K)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = gu.run_fused(dev, inp.K, stream=s)
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_page_permutation_keeps_raw_and_maps_slots():
+    _need_gpu()
+    inp = medium_inputs(seed=41)
+    a = gu.run_fused(gu.to_device(inp), inp.K)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(inp.P_phys)
+    kp = np.empty_like(inp.k_pages)
+    ks = np.empty_like(inp.k_scale)
+    kp[perm] = inp.k_pages
+    ks[perm] = inp.k_scale
+    moved = synth.Inputs(**{**inp.__dict__, "k_pages": kp, "k_scale": ks,
+                            "page_table": perm[inp.page_table].astype(np.int32)})
+    b = gu.run_fused(gu.to_device(moved), inp.K)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+    for r in range(inp.Q):
+        assert np.array_equal(b[1][r], expected_slots(b[0][r], moved.page_table))
+
+
+def test_all_equal_rows_select_first_k_positions():
+    _need_gpu()
+    inp = medium_inputs(seed=51)
+    inp.q[[0, 7, 19]] = 0
+    raw, slot, cnt, score = gu.run_fused(gu.to_device(inp), inp.K)
+    for r in (0, 7, 19):
+        st, en = int(inp.row_start[r]), int(inp.row_end[r])
+        if en - st > inp.K:
+            assert cnt[r] == inp.K
+            assert np.array_equal(raw[r], np.arange(st, st + inp.K))
+            assert np.all(score[r] == 0) and not np.any(np.signbit(score[r]))
+
+
+# --- fail closed -----------------------------------------------------------------------------
+
+def test_invalid_windows_and_pages_fail_closed():
+    _need_gpu()
+    inp = medium_inputs(seed=61)
+    inp.row_start[0], inp.row_end[0] = 10, 5          # end < start
+    inp.row_start[1], inp.row_end[1] = -3, 700        # negative start
+    inp.row_start[2], inp.row_end[2] = 0, inp.S + 1   # beyond the table
+    inp.page_table[7] = inp.P_phys + 4                # bad entry, page 7 = positions 448..511
+    inp.row_start[6], inp.row_end[6] = 400, 460       # short row touching page 7
+    inp.row_start[8], inp.row_end[8] = 0, 2000        # long row touching page 7
+    inp.row_start[9], inp.row_end[9] = 512, 1500      # long row after page 7: valid
+    dev = gu.to_device(inp)
+    mqa.mqa_fp4_status()
+    raw, slot, cnt, score = gu.run_fused(dev, inp.K)
+    assert mqa.mqa_fp4_status() == mqa.STATUS_BAD_WINDOW | mqa.STATUS_BAD_PAGE
+    assert mqa.mqa_fp4_status() == 0
+    for r, code in ((0, -1), (1, -1), (2, -1), (6, -2), (8, -2)):
+        assert cnt[r] == code and np.all(raw[r] == -1) and np.all(slot[r] == -1), r
+    check_rows(inp, [r for r in range(inp.Q) if r not in (0, 1, 2, 6, 8)], raw, slot, cnt, score,
+               where="fail-closed neighbours")
+
+
+def test_host_errors_write_nothing():
+    _need_gpu()
+    import torch
+    inp = medium_inputs(seed=71)
+    dev = gu.to_device(inp)
+    outs = mqa.alloc_outputs(inp.Q, 512, dev["q"].device)
+    for t in outs:
+        t.fill_(-7)
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.mqa_fp4_topk_prefill(dev["q"], dev["q_scale"], dev["k_pages"], dev["k_scale"], dev["weights"],
+                                 dev["page_table"], dev["row_start"], dev["row_end"], 513, *[
+                                     torch.empty((inp.Q, 513), dtype=torch.int32, device="cuda"),
+                                     torch.empty((inp.Q, 513), dtype=torch.int32, device="cuda"),
+                                     outs[2]])
+    assert e.value.code == -1
+    host = torch.from_numpy(inp.weights)                      # host memory where device is required
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.mqa_fp4_topk_prefill(dev["q"], dev["q_scale"], dev["k_pages"], dev["k_scale"], host,
+                                 dev["page_table"], dev["row_start"], dev["row_end"], 512, *outs)
+    assert e.value.code == -5
+    torch.cuda.synchronize()
+    for t in outs:
+        assert torch.all(t == -7)
+
+
+def test_graph_capture_is_rejected():
+    _need_gpu()
+    import torch
+    inp = medium_inputs(seed=81)
+    dev = gu.to_device(inp)
+    outs = mqa.alloc_outputs(inp.Q, inp.K, dev["q"].device)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        try:
+            mqa.mqa_fp4_topk_prefill(dev["q"], dev["q_scale"], dev["k_pages"], dev["k_scale"], dev["weights"],
+                                     dev["page_table"], dev["row_start"], dev["row_end"], inp.K, *outs,
+                                     stream=s)
+        except mqa.MQAError as e:
+            err = e
+        finally:
+            g.capture_end()
+    assert err is not None and err.code == -6
+
+
+def test_empty_batch_is_a_no_op():
+    _need_gpu()
+    inp = synth.make_inputs(0, 512, 512, 3)
+    raw, slot, cnt, _ = gu.run_fused(gu.to_device(inp), 512)
+    assert raw.shape == (0, 512) and cnt.shape == (0,)
+
+
+# --- special values -------------------------------------------------------------------------
+
+def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
+    _need_gpu()
+    inp = medium_inputs(seed=91, Q=8)
+    inp.weights[0] = 0
+    inp.weights[0, 3] = np.inf                  # +inf where d_3 > 0, NaN elsewhere
+    inp.weights[1, 10] = -np.inf
+    inp.weights[2, 40] = np.nan                 # every score NaN: first K positions
+    inp.weights[3, 0], inp.weights[3, 1] = np.inf, -np.inf
+    raw, slot, cnt, score = gu.run_fused(gu.to_device(inp), inp.K)
+    check_rows(inp, range(8), raw, slot, cnt, None, where="special weights")
+
+
+def test_logits_selector_total_order_on_special_value_arrays():
+    """Exact TopK over caller logits mixing NaN, +-inf, +-0 and ties: must equal
+    the oracle's selection exactly (no tolerance; the logits are given)."""
+    _need_gpu()
+    import torch
+    rng = np.random.default_rng(17)
+    Q, S = 12, 2048
+    pool = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 2.5, 1e-30, -1e-30, 3e38], np.float32)
+    lg = pool[rng.integers(0, pool.size, (Q, S))]
+    lg[::3] = np.where(rng.random((4, S)) < 0.5, lg[::3], rng.standard_normal((4, S)).astype(np.float32))
+    nanpay = np.array([0x7FC00001, 0xFFC00000, 0x7F800001], np.uint32).view(np.float32)
+    lg[5, ::7] = nanpay[rng.integers(0, 3, lg[5, ::7].shape)]
+    st = rng.integers(0, 600, Q).astype(np.int32)
+    en = np.minimum(st + rng.integers(300, 1600, Q), S).astype(np.int32)
+    pt = rng.permutation(S // 64).astype(np.int32)
+    for K in (512, 1024):
+        outs = mqa.alloc_outputs(Q, K, "cuda", with_score=True)
+        mqa.mqa_fp4_logits_topk(torch.from_numpy(lg).cuda(), torch.from_numpy(pt).cuda(), S // 64,
+                                torch.from_numpy(st).cuda(), torch.from_numpy(en).cuda(), K, *outs)
+        raw, slot, cnt, score = [t.cpu().numpy() for t in outs]
+        for r in range(Q):
+            n = int(en[r] - st[r])
+            c, want = oracle.select_topk(lg[r, st[r]:en[r]].astype(np.float64), int(st[r]), K)
+            assert cnt[r] == c, (K, r)
+            assert np.array_equal(raw[r], want), (K, r)
+            assert np.array_equal(slot[r], expected_slots(want, pt)), (K, r)
+            if n > K:
+                got = score[r].view(np.uint32)
+                ref = lg[r, want].view(np.uint32)          # logits are indexed by absolute position
+                isnan = np.isnan(lg[r, want])
+                assert np.array_equal(got[~isnan], ref[~isnan]) and np.all(np.isnan(score[r][isnan]))
+
+
+# --- the benchmark workloads at full size, sampled rows -------------------------------------
+
+@pytest.mark.parametrize("cfg,nrows", [(2, 6), (3, 4), (4, 4), (5, 4)])
+def test_full_size_workloads_sampled_rows(cfg, nrows):
+    _need_gpu()
+    inp = synth.make_config(cfg)
+    dev = gu.to_device(inp)
+    raw, slot, cnt, score = gu.run_fused(dev, inp.K)
+    n = inp.lengths()
+    long_rows = n > inp.K
+    assert np.all(cnt[long_rows] == inp.K) and np.all(cnt[~long_rows] == n[~long_rows])
+    # structural checks on every row: ascending, inside the window, slots mapped
+    assert np.all(np.diff(raw[long_rows], axis=1) > 0)
+    assert np.all(raw[long_rows] >= inp.row_start[long_rows, None])
+    assert np.all(raw[long_rows] < inp.row_end[long_rows, None])
+    assert np.array_equal(slot[long_rows], expected_slots(raw[long_rows], inp.page_table))
+    # tie rows (all-zero queries): the first K positions, scores exactly +0
+    for r in inp.tie_rows:
+        st = int(inp.row_start[r])
+        assert np.array_equal(raw[r], np.arange(st, st + inp.K)), r
+        assert np.all(score[r] == 0)
+    rows = synth.sample_rows(inp, nrows, seed=cfg)
+    check_rows(inp, rows, raw, slot, cnt, score, where=f"config {cfg}")
