@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FP4 paged-MQA indexer + exact TopK on one MI355X.
+
+One step = one call of mqa_fp4_topk_prefill (row preparation, fused MXFP4
+scoring + streaming TopK, exact split merge + page mapping) on the headline
+workload of "[FlyDSL] Add FP4 LiteTopK prefill operator" (ROCm/aiter PR
+5309), Validation table: V4-Pro shape, Q=8192 rows, H=64, D=128, K=1024,
+C4 context 196,608 (786,432 raw tokens), ragged causal prefill windows,
+shuffled pages, synthetic seeded FP4 data (fp4_mqa_scoring_amd/synth.py).
+
+Prints ONE JSON line. Besides the timed fused steps it measures, outside the
+timed region: the in-house dense comparator in alternating dense/fused pairs
+(the pages' protocol: 5 warmup + 15 measured pairs), the library's scratch
+bytes, and the CPU oracle on a bounded sample of rows (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FLOP_PER_PAIR = 2 * 64 * 128          # MXFP4 MFMA work per scored (row, position) pair
+VALU_PER_PAIR = 2 * 64                # integer ReLU + fp32 FMA per head
+MXFP4_PEAK = 10.1e15                  # MI355X dense MXFP4 MFMA, FLOP/s
+VALU_PEAK = 256 * 4 * 16 * 2.4e9      # lane-ops/s: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+HBM_PEAK = 8.0e12
+PAGES_LITETOPK_MS = {  # PR 5309 Validation table, MI355X, LiteTopK column
+    (8192, 196608, 1024): 10.6433, (8192, 131072, 1024): 7.4099, (8192, 65536, 1024): 4.1911,
+    (8192, 196608, 512): 10.4344, (8192, 131072, 512): 7.2235, (8192, 65536, 512): 3.9221,
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_topk_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("mqa_device.h", "mqa_kernels.hip"):
+        with open(os.path.join(ROOT, "fp4_mqa_scoring_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n: int):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float(0.0)
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for h in arr:
+            self.hip.hipEventDestroy(h)
+
+
+def cpu_baseline(inp, budget_s: float, seed: int):
+    """The oracle as it stands on this host's cores: whole rows of the same
+    workload (scores + full sort + page map) until the time budget is used."""
+    import oracle
+    rows = list(np.random.default_rng(seed).permutation(inp.Q))
+    pairs, t0, done = 0, time.perf_counter(), []
+    for r in rows:
+        n = int(inp.row_end[r] - inp.row_start[r])
+        oracle.topk_row(inp, int(r))
+        pairs += n
+        done.append(int(r))
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "scored pairs/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{len(done)} full rows of the same workload ({pairs} scored pairs, "
+                      f"{dt:.1f} s wall), float64 scores + full sort, OpenMP over positions"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="H", help="H (headline) or 1..5")
+    ap.add_argument("--pairs", type=int, default=15, help="alternating dense/fused pairs (0 = skip dense)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (for counter scaling)")
+    ap.add_argument("--splits", type=int, default=0, help="override context splits (0 = automatic)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the operator "
+              "shards by rows with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_mqa_scoring_amd as mqa
+    from fp4_mqa_scoring_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mqa.lib()                          # fail loudly if the HIP library is not built
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = args.workload if args.workload == "H" else int(args.workload)
+    inp = synth.make_config(cfg)
+    Q, S, K = inp.Q, inp.S, inp.K
+    pairs = inp.scored_pairs()
+    t = {n: torch.from_numpy(np.ascontiguousarray(getattr(inp, n))).to(dev)
+         for n in ("q", "q_scale", "k_pages", "k_scale", "weights", "page_table", "row_start", "row_end")}
+    out_raw, out_slot, out_count = mqa.alloc_outputs(Q, K, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def fused():
+        mqa.mqa_fp4_topk_prefill_ex(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"],
+                                    t["page_table"], t["row_start"], t["row_end"], K, out_raw, out_slot,
+                                    out_count, None, args.splits, stream=stream)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    evs = [ev.create(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mqa.mqa_fp4_set_stage_events(evs[i])
+        fused()
+    mqa.mqa_fp4_set_stage_events(None)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = [ev.elapsed_ms(e[0], e[3]) for e in evs]
+    kern_ms = [ev.elapsed_ms(e[1], e[2]) for e in evs]
+    prep_ms = [ev.elapsed_ms(e[0], e[1]) for e in evs]
+    merge_ms = [ev.elapsed_ms(e[2], e[3]) for e in evs]
+    for e in evs:
+        ev.destroy(e)
+    status = mqa.mqa_fp4_status(stream)
+    counts = out_count.cpu().numpy()
+    n = inp.lengths()
+    ok = bool(np.all(counts[n > K] == K) and np.all(counts[n <= K] == n[n <= K]) and status == 0)
+
+    ms_step = wall_ms                   # synchronized wall clock of the timed steps
+    kern = float(np.mean(kern_ms))
+    value = pairs / (ms_step * 1e-3)
+    kern_flops = pairs * FLOP_PER_PAIR / (kern * 1e-3)
+    kern_valu = pairs * VALU_PER_PAIR / (kern * 1e-3)
+
+    # alternating dense / fused pairs, outside the timed region
+    dense = None
+    if args.pairs > 0:
+        logits = torch.empty((Q, S), dtype=torch.float32, device=dev)
+        d_out = mqa.alloc_outputs(Q, K, dev)
+
+        def dense_call():
+            mqa.mqa_fp4_dense_topk_prefill(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"],
+                                           t["page_table"], t["row_start"], t["row_end"], K, logits, *d_out,
+                                           stream=stream)
+        dms, fms = [], []
+        for i in range(5 + args.pairs):
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s2 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            dense_call()
+            s1.record(stream)
+            fused()
+            s2.record(stream)
+            torch.cuda.synchronize()
+            if i >= 5:
+                dms.append(s0.elapsed_time(s1))
+                fms.append(s1.elapsed_time(s2))
+        same = bool(torch.equal(d_out[0], out_raw) and torch.equal(d_out[2], out_count))
+        dense = {"dense_ms_median": float(np.median(dms)), "fused_ms_median": float(np.median(fms)),
+                 "pairs": args.pairs, "dense_equals_fused": same,
+                 "dense_logits_bytes": Q * S * 4}
+        del logits
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("workload") == str(args.workload):
+            traffic = tr.get("bytes_per_launch")
+
+    line = {
+        "metric": "ms/call + scored pairs/s (% MXFP4 MFMA peak), Q=8192 C4=196608 K=1024",
+        "value": value,
+        "unit": "scored pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": inp.name, "Q": Q, "c4_context": S, "K": K, "heads": 64, "head_dim": 128,
+                   "page_size": 64, "windows": "ragged causal, end_i = S - floor((Q-1-i)/4)",
+                   "scored_pairs": pairs, "splits": args.splits or "auto"},
+        "roofline": {"bound": "alu", "achieved": kern_valu / 1e12, "peak": VALU_PEAK / 1e12,
+                     "unit": "Tops/s", "frac": kern_valu / VALU_PEAK, "traffic": traffic,
+                     "kernel": "fused_topk_kernel",
+                     "mfma_tflops": kern_flops / 1e12, "mfma_frac": kern_flops / MXFP4_PEAK},
+        "mxfp4_tflops_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / 1e12,
+        "mxfp4_peak_frac_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / MXFP4_PEAK,
+        "stage_ms": {"row_prep": float(np.mean(prep_ms)), "fused_topk_kernel": kern,
+                     "merge_emit": float(np.mean(merge_ms)), "call_events": float(np.mean(call_ms))},
+        "scratch_bytes": mqa.mqa_fp4_topk_scratch_bytes(Q, K, 0),
+        "dense_comparator": dense,
+        "checks_ok": ok,
+    }
+    key = (Q, S, K)
+    if key in PAGES_LITETOPK_MS and args.workload == "H":
+        line["vs_baseline"] = PAGES_LITETOPK_MS[key] / ms_step
+    if args.cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, seed=1)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

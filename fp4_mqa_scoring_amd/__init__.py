@@ -40,6 +40,10 @@ def lib() -> ctypes.CDLL:
     """The loaded HIP library (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        try:  # share torch's HIP runtime (same SONAME) so torch streams and memory are valid here
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
                                "`python -m fp4_mqa_scoring_amd.build` (or __graft_entry__.build())")
@@ -58,9 +62,10 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_error_string.argtypes = [i32]
         L.mqa_fp4_error_string.restype = ctypes.c_char_p
         L.mqa_fp4_abi_version.argtypes = []
+        L.mqa_fp4_set_stage_events.argtypes = [P, i32]
         for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
-                     "mqa_fp4_status", "mqa_fp4_abi_version"):
+                     "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -238,3 +243,13 @@ def mqa_fp4_status(stream=None, device=None) -> int:
 
 def mqa_fp4_abi_version() -> int:
     return int(lib().mqa_fp4_abi_version())
+
+
+def mqa_fp4_set_stage_events(events) -> None:
+    """Measurement hook: ``events`` is a ctypes array of 4 hipEvent_t handles
+    (or None to turn the hook off); see the C header."""
+    if events is None:
+        _rc(lib().mqa_fp4_set_stage_events(None, 0), "mqa_fp4_set_stage_events")
+    else:
+        _rc(lib().mqa_fp4_set_stage_events(ctypes.cast(events, ctypes.c_void_p), len(events)),
+            "mqa_fp4_set_stage_events")

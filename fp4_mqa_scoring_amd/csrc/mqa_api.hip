@@ -192,6 +192,13 @@ struct Scratch {
   }
 };
 
+// Stage events of the measurement hook (per host thread).
+thread_local void* const* t_stage_events = nullptr;
+
+void record_stage(int i, hipStream_t st) {
+  if (t_stage_events) (void)hipEventRecord(static_cast<hipEvent_t>(t_stage_events[i]), st);
+}
+
 int32_t hip_rc(hipError_t e) {
   if (e == hipSuccess) return MQA_OK;
   (void)hipGetLastError();
@@ -225,9 +232,13 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   int32_t* row_state = reinterpret_cast<int32_t*>(base + lay.state_off);
   uint64_t* keys = reinterpret_cast<uint64_t*>(base + lay.keys_off);
   int32_t* counts = reinterpret_cast<int32_t*>(base + lay.count_off);
+  record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  record_stage(1, st);
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_fused(p, row_state, splits, keys, counts, st));
+  record_stage(2, st);
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_merge(p, row_state, splits, keys, counts, st));
+  record_stage(3, st);
   return rc;
 }
 
@@ -284,9 +295,13 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
   int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  record_stage(1, st);
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
+  record_stage(2, st);
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
+  record_stage(3, st);
   return rc;
 }
 
@@ -378,6 +393,16 @@ int32_t mqa_fp4_status(void* stream, int32_t* status) {
   rc = guard.enter(dev);
   if (rc != MQA_OK) return rc;
   return hip_rc(mqa::status_take(st, status));
+}
+
+int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n) {
+  if (events == nullptr || n == 0) {
+    t_stage_events = nullptr;
+    return MQA_OK;
+  }
+  if (n != 4) return MQA_ERR_BAD_SIZE;
+  t_stage_events = events;
+  return MQA_OK;
 }
 
 const char* mqa_fp4_error_string(int32_t code) {

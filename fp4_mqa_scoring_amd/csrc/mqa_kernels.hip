@@ -88,23 +88,35 @@ __global__ void __launch_bounds__(256) row_prep_kernel(
 // ---------------------------------------------------------------------------
 struct TileLoader {
   v4i c0, c1, sc;
+  int32_t code_entry, scale_entry;   // raw page-table entries fetched ahead
+  int64_t code_page, scale_page;     // validated physical pages of the tile to load next
 
-  __device__ __forceinline__ static int64_t phys(const int32_t* pt, int64_t P_log, int64_t P_phys,
-                                                int64_t lp) {
-    if (lp >= P_log) return -1;
-    const int64_t e = pt[lp];
+  __device__ __forceinline__ static int64_t valid_or_neg(int32_t e, int64_t P_phys) {
     return (e >= 0 && e < P_phys) ? e : -1;
   }
 
-  // Global -> registers for score block t. Pages beyond the table or with an
-  // out-of-range entry are not read (their rows were rejected by row_prep).
-  __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale,
-                                       const int32_t* pt, int64_t P_log, int64_t P_phys, int t) {
+  // Page-table entries of score block t for this thread's code chunk and (first
+  // wave) scale chunk; -1 beyond the table. Issued two blocks ahead of use.
+  __device__ __forceinline__ void fetch_entries(const int32_t* pt, int64_t P_log, int t) {
     const int tid = threadIdx.x;
-    const int pi = tid >> 7, within = tid & 127;
-    const int64_t e = phys(pt, P_log, P_phys, static_cast<int64_t>(t) * kTilePages + pi);
-    if (e >= 0) {
-      const v4i* src = reinterpret_cast<const v4i*>(k_pages + static_cast<size_t>(e) * kPage * kVecBytes +
+    const int64_t lp = static_cast<int64_t>(t) * kTilePages + (tid >> 7);
+    code_entry = lp < P_log ? pt[lp] : -1;
+    const int64_t slp = static_cast<int64_t>(t) * kTilePages + ((tid & 63) >> 4);
+    scale_entry = slp < P_log ? pt[slp] : -1;
+  }
+
+  __device__ __forceinline__ void resolve(int64_t P_phys) {
+    code_page = valid_or_neg(code_entry, P_phys);
+    scale_page = valid_or_neg(scale_entry, P_phys);
+  }
+
+  // Global -> registers for the resolved score block. Pages with an
+  // out-of-range entry are not read (their rows were rejected by row_prep).
+  __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale) {
+    const int tid = threadIdx.x;
+    const int within = tid & 127;
+    if (code_page >= 0) {
+      const v4i* src = reinterpret_cast<const v4i*>(k_pages + static_cast<size_t>(code_page) * kPage * kVecBytes +
                                                     static_cast<size_t>(within) * 32);
       c0 = src[0];
       c1 = src[1];
@@ -113,10 +125,10 @@ struct TileLoader {
       c1 = v4i{0, 0, 0, 0};
     }
     if (tid < 64) {
-      const int spi = tid >> 4, off = (tid & 15) * 16;
-      const int64_t se = phys(pt, P_log, P_phys, static_cast<int64_t>(t) * kTilePages + spi);
-      sc = se >= 0 ? *reinterpret_cast<const v4i*>(k_scale + static_cast<size_t>(se) * kPage * kVecScales + off)
-                   : v4i{0, 0, 0, 0};
+      const int off = (tid & 15) * 16;
+      sc = scale_page >= 0
+               ? *reinterpret_cast<const v4i*>(k_scale + static_cast<size_t>(scale_page) * kPage * kVecScales + off)
+               : v4i{0, 0, 0, 0};
     }
   }
 
@@ -129,6 +141,27 @@ struct TileLoader {
     *reinterpret_cast<v4i*>(dst + 16 * ((2 * half) ^ sw)) = c0;
     *reinterpret_cast<v4i*>(dst + 16 * ((2 * half + 1) ^ sw)) = c1;
     if (tid < 64) *reinterpret_cast<v4i*>(s_scales + (tid >> 4) * (kPage * kVecScales) + (tid & 15) * 16) = sc;
+  }
+
+  // Prologue: block t_begin into LDS buffer t_begin & 1, entries of the next
+  // block in flight.
+  __device__ __forceinline__ void prologue(const uint8_t* k_pages, const uint8_t* k_scale, const int32_t* pt,
+                                           int64_t P_log, int64_t P_phys, int t_begin, int t_end,
+                                           uint8_t* s_codes, uint8_t* s_scales) {
+    fetch_entries(pt, P_log, t_begin);
+    resolve(P_phys);
+    load(k_pages, k_scale);
+    if (t_begin + 1 < t_end) fetch_entries(pt, P_log, t_begin + 1);
+    store(s_codes, s_scales);
+  }
+
+  // Start of block t: data loads of block t+1 (entries fetched one block ago)
+  // and page-table loads of block t+2.
+  __device__ __forceinline__ void advance(const uint8_t* k_pages, const uint8_t* k_scale, const int32_t* pt,
+                                          int64_t P_log, int64_t P_phys, int t, int t_end) {
+    resolve(P_phys);
+    load(k_pages, k_scale);
+    if (t + 2 < t_end) fetch_entries(pt, P_log, t + 2);
   }
 };
 
@@ -215,16 +248,18 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fused_topk_kernel(ScanArgs a, 
   uint64_t gate = 0;     // keys > gate may still be in this split's TopK
   bool failed = false;
 
+  // query operands and weights must be in registers before the scan loop
+  __builtin_amdgcn_s_waitcnt(0);
   TileLoader ld;
   if (t_begin < t_end) {
-    ld.load(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin);
-    ld.store(s_codes[t_begin & 1], s_scales[t_begin & 1]);
+    ld.prologue(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin, t_end, s_codes[t_begin & 1],
+                s_scales[t_begin & 1]);
     __syncthreads();
   }
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < t_end;
-    if (more) ld.load(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t + 1);
+    if (more) ld.advance(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t, t_end);
     const int tb = t * kTile;
     if (active && tb < end && tb + kTile > start) {
 #pragma unroll 1
@@ -294,16 +329,18 @@ __global__ void __launch_bounds__(kCtaThreads, 1) dense_score_kernel(ScanArgs a,
               a.weights + static_cast<size_t>(row) * kHeads, lane);
   float* out = logits + static_cast<size_t>(row) * (a.P_log * kPage);
 
+  // query operands and weights must be in registers before the scan loop
+  __builtin_amdgcn_s_waitcnt(0);
   TileLoader ld;
   if (t_begin < t_end) {
-    ld.load(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin);
-    ld.store(s_codes[t_begin & 1], s_scales[t_begin & 1]);
+    ld.prologue(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin, t_end, s_codes[t_begin & 1],
+                s_scales[t_begin & 1]);
     __syncthreads();
   }
   for (int t = t_begin; t < t_end; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < t_end;
-    if (more) ld.load(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t + 1);
+    if (more) ld.advance(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t, t_end);
     const int tb = t * kTile;
     if (active && tb < end && tb + kTile > start) {
 #pragma unroll 1
