@@ -25,6 +25,8 @@ ERRORS = {
 ROW_BAD_WINDOW, ROW_BAD_PAGE, ROW_UNDERFILL, ROW_SELECTOR = -1, -2, -3, -4
 STATUS_BAD_WINDOW, STATUS_BAD_PAGE, STATUS_UNDERFILL, STATUS_SELECTOR = 1, 2, 4, 8
 FLAG_SPLITS_MASK = 0xFF
+FLAG_NO_PREFILTER = 0x100
+FLAG_FORCE_UNDERFILL = 0x200
 
 
 class MQAError(RuntimeError):

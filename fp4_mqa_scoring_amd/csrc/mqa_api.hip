@@ -132,10 +132,11 @@ int32_t check_capture(hipStream_t st) {
   return cs == hipStreamCaptureStatusNone ? MQA_OK : MQA_ERR_CAPTURING;
 }
 
-int32_t auto_splits(int64_t Q, int cus) {
+// Context splits per row tile: enough CTAs for `per_cu` of them per CU.
+int32_t auto_splits(int64_t Q, int cus, int per_cu = 2) {
   const int64_t tiles = (Q + kRowsPerCta - 1) / kRowsPerCta;
   if (tiles <= 0) return 1;
-  int64_t s = (2 * static_cast<int64_t>(cus) + tiles - 1) / tiles;
+  int64_t s = (per_cu * static_cast<int64_t>(cus) + tiles - 1) / tiles;
   if (s < 1) s = 1;
   if (s > kMaxAutoSplits) s = kMaxAutoSplits;
   return static_cast<int32_t>(s);
@@ -144,15 +145,22 @@ int32_t auto_splits(int64_t Q, int cus) {
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct FusedScratch {
-  size_t state_off, keys_off, count_off, total;
+  size_t state_off, gate_off, count_off, list_off, listn_off, fbcnt_off, cand_off, total;
 };
 
-FusedScratch fused_scratch_layout(int64_t Q, int32_t K, int32_t splits) {
+// Independent of the context length: O(Q) bookkeeping plus a bounded
+// candidate buffer of candidate_cap(K) keys per row.
+FusedScratch fused_scratch_layout(int64_t Q, int32_t K) {
+  const size_t q = static_cast<size_t>(Q);
   FusedScratch s;
   s.state_off = 0;
-  s.keys_off = align_up(static_cast<size_t>(Q) * sizeof(int32_t));
-  s.count_off = s.keys_off + align_up(static_cast<size_t>(Q) * splits * K * sizeof(uint64_t));
-  s.total = s.count_off + align_up(static_cast<size_t>(Q) * splits * sizeof(int32_t));
+  s.gate_off = s.state_off + align_up(q * sizeof(int32_t));
+  s.count_off = s.gate_off + align_up(q * sizeof(uint64_t));
+  s.list_off = s.count_off + align_up(q * sizeof(uint32_t));
+  s.listn_off = s.list_off + align_up(q * sizeof(int32_t));
+  s.fbcnt_off = s.listn_off + align_up(sizeof(int32_t));
+  s.cand_off = s.fbcnt_off + align_up(q * 4 * sizeof(int32_t));
+  s.total = s.cand_off + align_up(q * static_cast<size_t>(mqa::candidate_cap(K)) * sizeof(uint64_t));
   return s;
 }
 
@@ -207,7 +215,9 @@ int32_t hip_rc(hipError_t e) {
 
 int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   if (p.K != 512 && p.K != 1024) return MQA_ERR_UNSUPPORTED_K;
-  if (flags & ~static_cast<uint32_t>(MQA_FLAG_SPLITS_MASK)) return MQA_ERR_BAD_FLAGS;
+  const uint32_t known = MQA_FLAG_SPLITS_MASK | MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL;
+  if (flags & ~known) return MQA_ERR_BAD_FLAGS;
+  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
   int32_t rc = check_sizes(p.Q, p.P_phys, p.P_log);
   if (rc != MQA_OK) return rc;
   const bool rows = p.Q > 0;
@@ -223,21 +233,28 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   if (rc != MQA_OK) return rc;
   if (!rows) return MQA_OK;
   const int32_t splits = (flags & MQA_FLAG_SPLITS_MASK) ? static_cast<int32_t>(flags & MQA_FLAG_SPLITS_MASK)
-                                                        : auto_splits(p.Q, info.cus);
-  const FusedScratch lay = fused_scratch_layout(p.Q, p.K, splits);
+                                                        : auto_splits(p.Q, info.cus, 4);
+  const int calib_mode = (flags & MQA_FLAG_NO_PREFILTER) ? 1 : (flags & MQA_FLAG_FORCE_UNDERFILL) ? 2 : 0;
+  const FusedScratch lay = fused_scratch_layout(p.Q, p.K);
   Scratch scratch;
   rc = scratch.alloc(lay.total, st);
   if (rc != MQA_OK) return rc;
   char* base = static_cast<char*>(scratch.p);
-  int32_t* row_state = reinterpret_cast<int32_t*>(base + lay.state_off);
-  uint64_t* keys = reinterpret_cast<uint64_t*>(base + lay.keys_off);
-  int32_t* counts = reinterpret_cast<int32_t*>(base + lay.count_off);
+  mqa::GatedScratch g;
+  g.row_state = reinterpret_cast<int32_t*>(base + lay.state_off);
+  g.gate = reinterpret_cast<uint64_t*>(base + lay.gate_off);
+  g.count = reinterpret_cast<uint32_t*>(base + lay.count_off);
+  g.fb_list = reinterpret_cast<int32_t*>(base + lay.list_off);
+  g.fb_count = reinterpret_cast<int32_t*>(base + lay.listn_off);
+  g.fb_cnt = reinterpret_cast<int32_t*>(base + lay.fbcnt_off);
+  g.cand = reinterpret_cast<uint64_t*>(base + lay.cand_off);
   record_stage(0, st);
-  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  rc = hip_rc(mqa::launch_row_prep(p, 0, g.row_state, g.fb_count, st));
   record_stage(1, st);
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_fused(p, row_state, splits, keys, counts, st));
-  record_stage(2, st);
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_merge(p, row_state, splits, keys, counts, st));
+  for (int stage = 0; stage < 5 && rc == MQA_OK; ++stage) {
+    rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_mode, stage, st));
+    if (stage == 1) record_stage(2, st);
+  }
   record_stage(3, st);
   return rc;
 }
@@ -296,7 +313,7 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   if (rc != MQA_OK) return rc;
   int32_t* row_state = static_cast<int32_t*>(scratch.p);
   record_stage(0, st);
-  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   record_stage(1, st);
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
   record_stage(2, st);
@@ -329,7 +346,7 @@ int32_t mqa_fp4_dense_logits(const uint8_t* q, const uint8_t* q_scale, int64_t n
   rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
   int32_t* row_state = static_cast<int32_t*>(scratch.p);
-  rc = hip_rc(mqa::launch_row_prep(p, 1, row_state, st));
+  rc = hip_rc(mqa::launch_row_prep(p, 1, row_state, nullptr, st));
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
   return rc;
 }
@@ -359,7 +376,7 @@ int32_t mqa_fp4_logits_topk(const float* logits, int64_t num_rows, const int32_t
   rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
   int32_t* row_state = static_cast<int32_t*>(scratch.p);
-  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, st));
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
   return rc;
 }
@@ -380,7 +397,7 @@ int64_t mqa_fp4_topk_scratch_bytes(int64_t num_rows, int32_t K, int32_t device) 
   const int32_t rc = device_info(device, &info);
   if (rc != MQA_OK) return rc;
   if (num_rows == 0) return 0;
-  return static_cast<int64_t>(fused_scratch_layout(num_rows, K, auto_splits(num_rows, info.cus)).total);
+  return static_cast<int64_t>(fused_scratch_layout(num_rows, K).total);
 }
 
 int32_t mqa_fp4_status(void* stream, int32_t* status) {

@@ -1,19 +1,29 @@
 // HIP kernels of the FP4 paged-MQA prefill indexer with exact TopK (gfx950).
 //
-// Pipeline of the fused path (all on the caller's stream):
-//   row_prep        validate windows and pages, answer short rows (length <= K)
-//   fused_topk      per (8-row tile, context split): stream 256-position score
-//                   blocks through LDS, MXFP4 MFMA scoring, ReLU + head-weighted
-//                   sum in registers, exact streaming selection in a bounded LDS
-//                   pool per row; emit <= K keys per (row, split)
-//   merge_emit      per row: exact TopK over the split candidates, ascending
-//                   order, raw -> physical page mapping
-// The dense comparator replaces fused_topk + merge_emit by dense_score (fp32
+// Fused path (all on the caller's stream, no host synchronisation):
+//   row_prep     validate windows and pages, answer short rows (length <= K)
+//   calib        per row: score a sample (every 16th position of the row tile's
+//                range), keep the sample's exact top-k' and derive the gate T0 =
+//                its k'-th key
+//   scan         per (8-row tile, context split): score every 256-position block
+//                with MXFP4 MFMA, ReLU + head-weighted sum in registers; keys >= T0
+//                are staged per wave in LDS and appended to the row's bounded
+//                global candidate buffer
+//   merge        per row: the candidates are exactly the window's keys >= T0; if
+//                there are at least K of them their top-K is the row's top-K:
+//                exact radix select, ascending order, raw -> physical mapping.
+//                Rows with fewer than K (gate too high) or more than the buffer
+//                holds go to a device-side list
+//   fallback     listed rows only: exact streaming TopK without a gate in bounded
+//                LDS pools, then the same exact merge; costs one empty launch pair
+//                when the list is empty
+// The dense comparator replaces everything after row_prep by dense_score (fp32
 // logits [Q, S]) + logits_topk.
 //
 // Sources: "[FlyDSL] Add FP4 LiteTopK prefill operator" (ROCm/aiter PR 5309),
-// Implementation; "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK" (ROCm/aiter
-// PR 5282), Changes and Scope.
+// Implementation (calibrated candidate filtering, stable exact TopK, page
+// mapping, fail closed); "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
+// (ROCm/aiter PR 5282), Changes and Scope.
 #include "mqa_device.h"
 #include "mqa_launch.h"
 
@@ -30,14 +40,16 @@ __device__ int32_t g_status;
 // mode 0 (TopK): invalid rows -> -1 outputs and a negative count; short rows ->
 //   positions start..end-1 then -1, count = length; long rows -> kRowLong.
 // mode 1 (logits only): every valid non-empty row -> kRowLong, no outputs.
+// Block 0 also clears the fallback list counter of this call (if any).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) row_prep_kernel(
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ row_end,
     const int32_t* __restrict__ page_table, int64_t P_log, int64_t P_phys, int32_t K, int mode,
     int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
-    float* __restrict__ out_score, int32_t* __restrict__ row_state) {
+    float* __restrict__ out_score, int32_t* __restrict__ row_state, int32_t* __restrict__ fb_count) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
+  if (row == 0 && tid == 0 && fb_count) *fb_count = 0;
   const int64_t start = row_start[row], end = row_end[row];
   int code = 0;
   if (start < 0 || end < start || end > kPage * P_log) {
@@ -80,23 +92,23 @@ __global__ void __launch_bounds__(256) row_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Score-block streaming shared by the fused and the dense scorer.
-// One CTA = 8 query rows (one per wave) x one contiguous range of 256-position
-// score blocks. Each block (4 pages = 16 KiB codes + 1 KiB scales) is gathered
-// through the page table with coalesced 32-byte-per-thread loads into registers
-// one block ahead, then written to a double-buffered LDS image.
+// Score-block streaming shared by all scoring kernels. One CTA = 8 query rows
+// (one per wave) x a sequence of 256-position score blocks. Each block (4 pages
+// = 16 KiB codes + 1 KiB scales) is gathered through the page table with
+// coalesced 32-byte-per-thread loads into registers one block ahead (page-table
+// entries two blocks ahead), then written to a double-buffered LDS image.
 // ---------------------------------------------------------------------------
 struct TileLoader {
   v4i c0, c1, sc;
   int32_t code_entry, scale_entry;   // raw page-table entries fetched ahead
-  int64_t code_page, scale_page;     // validated physical pages of the tile to load next
+  int64_t code_page, scale_page;     // validated physical pages of the block to load next
 
   __device__ __forceinline__ static int64_t valid_or_neg(int32_t e, int64_t P_phys) {
     return (e >= 0 && e < P_phys) ? e : -1;
   }
 
   // Page-table entries of score block t for this thread's code chunk and (first
-  // wave) scale chunk; -1 beyond the table. Issued two blocks ahead of use.
+  // wave) scale chunk; -1 beyond the table.
   __device__ __forceinline__ void fetch_entries(const int32_t* pt, int64_t P_log, int t) {
     const int tid = threadIdx.x;
     const int64_t lp = static_cast<int64_t>(t) * kTilePages + (tid >> 7);
@@ -142,27 +154,6 @@ struct TileLoader {
     *reinterpret_cast<v4i*>(dst + 16 * ((2 * half + 1) ^ sw)) = c1;
     if (tid < 64) *reinterpret_cast<v4i*>(s_scales + (tid >> 4) * (kPage * kVecScales) + (tid & 15) * 16) = sc;
   }
-
-  // Prologue: block t_begin into LDS buffer t_begin & 1, entries of the next
-  // block in flight.
-  __device__ __forceinline__ void prologue(const uint8_t* k_pages, const uint8_t* k_scale, const int32_t* pt,
-                                           int64_t P_log, int64_t P_phys, int t_begin, int t_end,
-                                           uint8_t* s_codes, uint8_t* s_scales) {
-    fetch_entries(pt, P_log, t_begin);
-    resolve(P_phys);
-    load(k_pages, k_scale);
-    if (t_begin + 1 < t_end) fetch_entries(pt, P_log, t_begin + 1);
-    store(s_codes, s_scales);
-  }
-
-  // Start of block t: data loads of block t+1 (entries fetched one block ago)
-  // and page-table loads of block t+2.
-  __device__ __forceinline__ void advance(const uint8_t* k_pages, const uint8_t* k_scale, const int32_t* pt,
-                                          int64_t P_log, int64_t P_phys, int t, int t_end) {
-    resolve(P_phys);
-    load(k_pages, k_scale);
-    if (t + 2 < t_end) fetch_entries(pt, P_log, t + 2);
-  }
 };
 
 struct ScanArgs {
@@ -181,11 +172,31 @@ struct ScanArgs {
   int32_t splits;
 };
 
-// CTA-uniform score-block range [t_begin, t_end) of this split over the union
-// of the CTA's active row windows; returns false when the CTA has no active row.
-__device__ __forceinline__ bool cta_tile_range(const ScanArgs& a, int32_t* s_lo, int32_t* s_hi,
-                                               bool active, int start, int end, int wave, int lane,
-                                               int* t_begin, int* t_end) {
+// Candidate buffers of the gated path (scratch of one call).
+struct CandArgs {
+  uint64_t* gate;        // [Q] keys > gate are candidates
+  uint32_t* count;       // [Q] candidates appended (may exceed cap: overflow)
+  uint64_t* cand;        // [Q, cap]
+  int32_t* fb_list;      // [Q] rows sent to the exact fallback
+  int32_t* fb_count;     // [1]
+  int32_t* fb_cnt;       // [Q, 4] per (row, fallback split) key counts
+  int32_t cap;
+};
+
+constexpr int kCalStride = 16;       // the calibration samples every 16th position
+constexpr int kCalCap = 512;         // calibration pool per row
+constexpr int kStageCap = 256;       // per-wave LDS staging of candidate keys
+
+// Score blocks [a, a+n) visited by a CTA.
+struct BlockSeq {
+  int a, n;
+  __device__ __forceinline__ int tile(int i) const { return a + i; }
+};
+
+// CTA-uniform block range [u0, u1) covering the union of the CTA's active row
+// windows; false when no row of the CTA is active.
+__device__ __forceinline__ bool row_tile_range(int32_t* s_lo, int32_t* s_hi, bool active, int start, int end,
+                                               int wave, int lane, int* u0, int* u1) {
   if (lane == 0) {
     s_lo[wave] = active ? start : INT_MAX;
     s_hi[wave] = active ? end : INT_MIN;
@@ -197,31 +208,157 @@ __device__ __forceinline__ bool cta_tile_range(const ScanArgs& a, int32_t* s_lo,
     lo = min(lo, s_lo[i]);
     hi = max(hi, s_hi[i]);
   }
+  __syncthreads();   // s_lo / s_hi may be reused right after
   if (lo >= hi) return false;
-  const int u0 = lo / kTile, u1 = (hi + kTile - 1) / kTile;
-  const int64_t nt = u1 - u0;
-  *t_begin = u0 + static_cast<int>(nt * blockIdx.y / a.splits);
-  *t_end = u0 + static_cast<int>(nt * (blockIdx.y + 1) / a.splits);
+  *u0 = lo / kTile;
+  *u1 = (hi + kTile - 1) / kTile;
   return true;
 }
 
+__device__ __forceinline__ BlockSeq split_range(int u0, int u1, int split, int splits) {
+  const int64_t nt = u1 - u0;
+  const int a = u0 + static_cast<int>(nt * split / splits);
+  const int b = u0 + static_cast<int>(nt * (split + 1) / splits);
+  return BlockSeq{a, b - a};
+}
+
+// Gathers "sample blocks": block v holds the 256 positions base + 16 * (256 v + p),
+// p = 0..255 (base = first position of the row tile's range, a multiple of 256),
+// i.e. every 16th position, from 64 different pages. Same LDS image as a score
+// block, so score64() applies unchanged.
+struct SampleLoader {
+  v4i c0, c1;
+  int32_t sc;
+  int32_t code_entry, scale_entry;
+  int64_t code_page, scale_page;
+  int u0;
+
+  __device__ __forceinline__ void fetch_entries(const int32_t* pt, int64_t P_log, int v) {
+    const int tid = threadIdx.x;
+    const int64_t base_page = static_cast<int64_t>(u0) * kTilePages + static_cast<int64_t>(v) * 64;
+    const int64_t lp = base_page + ((tid >> 1) >> 2);
+    code_entry = lp < P_log ? pt[lp] : -1;
+    const int64_t slp = base_page + ((tid & 255) >> 2);
+    scale_entry = slp < P_log ? pt[slp] : -1;
+  }
+
+  __device__ __forceinline__ void resolve(int64_t P_phys) {
+    code_page = TileLoader::valid_or_neg(code_entry, P_phys);
+    scale_page = TileLoader::valid_or_neg(scale_entry, P_phys);
+  }
+
+  __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale) {
+    const int tid = threadIdx.x;
+    const int p = tid >> 1, half = tid & 1;
+    if (code_page >= 0) {
+      const v4i* src = reinterpret_cast<const v4i*>(k_pages + static_cast<size_t>(code_page) * kPage * kVecBytes +
+                                                    static_cast<size_t>(16 * (p & 3)) * kVecBytes + 32 * half);
+      c0 = src[0];
+      c1 = src[1];
+    } else {
+      c0 = v4i{0, 0, 0, 0};
+      c1 = v4i{0, 0, 0, 0};
+    }
+    if (tid < 256) {
+      const int ps = tid;
+      sc = scale_page >= 0 ? *reinterpret_cast<const int32_t*>(k_scale + static_cast<size_t>(scale_page) * kPage * kVecScales +
+                                                               static_cast<size_t>(16 * (ps & 3)) * kVecScales)
+                           : 0;
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* s_codes, uint8_t* s_scales) const {
+    const int tid = threadIdx.x;
+    const int p = tid >> 1, half = tid & 1;
+    const int sw = chunk_swizzle(p);
+    uint8_t* dst = s_codes + p * kVecBytes;
+    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half) ^ sw)) = c0;
+    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half + 1) ^ sw)) = c1;
+    if (tid < 256) *reinterpret_cast<int32_t*>(s_scales + tid * kVecScales) = sc;
+  }
+};
+
+// Streams the CTA's block sequence through LDS and calls
+// body(tile, s_codes, s_scales) for every block, for every wave (uniformly).
+template <class Loader, class Body>
+__device__ __forceinline__ void stream_with(Loader& ld, const ScanArgs& a, const BlockSeq& seq,
+                                            uint8_t (*s_codes)[kTile * kVecBytes],
+                                            uint8_t (*s_scales)[kTile * kVecScales], Body&& body) {
+  if (seq.n <= 0) return;
+  ld.fetch_entries(a.page_table, a.P_log, seq.tile(0));
+  ld.resolve(a.P_phys);
+  ld.load(a.k_pages, a.k_scale);
+  if (seq.n > 1) ld.fetch_entries(a.page_table, a.P_log, seq.tile(1));
+  ld.store(s_codes[0], s_scales[0]);
+  __syncthreads();
+  for (int i = 0; i < seq.n; ++i) {
+    const int buf = i & 1;
+    const bool more = i + 1 < seq.n;
+    if (more) {
+      ld.resolve(a.P_phys);
+      ld.load(a.k_pages, a.k_scale);
+      if (i + 2 < seq.n) ld.fetch_entries(a.page_table, a.P_log, seq.tile(i + 2));
+    }
+    body(seq.tile(i), s_codes[buf], s_scales[buf]);
+    if (more) ld.store(s_codes[buf ^ 1], s_scales[buf ^ 1]);
+    __syncthreads();
+  }
+}
+
+template <class Body>
+__device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t (*s_codes)[kTile * kVecBytes],
+                                              uint8_t (*s_scales)[kTile * kVecScales], Body&& body) {
+  TileLoader ld;
+  stream_with(ld, a, seq, s_codes, s_scales, static_cast<Body&&>(body));
+}
+
+// Calls f(p0, blk) for each 64-position block of score block t that intersects
+// [start, end).
+template <class F>
+__device__ __forceinline__ void for_blocks_in_window(int t, int start, int end, F&& f) {
+  const int tb = t * kTile;
+  if (tb >= end || tb + kTile <= start) return;
+#pragma unroll 1
+  for (int blk = 0; blk < kTile / 64; ++blk) {
+    const int p0 = tb + 64 * blk;
+    if (p0 >= end || p0 + 64 <= start) continue;
+    f(p0, blk);
+  }
+}
+
+// Smallest key of pool[0..n) (n >= 1).
+__device__ __forceinline__ uint64_t wave_min_key(const uint64_t* pool, int n, int lane) {
+  uint64_t m = ~0ull;
+  for (int i = lane; i < n; i += 64) m = min(m, pool[i]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = min(m, shfl_xor_u64(m, o));
+  return m;
+}
+
+// Candidates the sample must keep: x + 4 sqrt(x) + 8 where x = K m / n is the
+// expected number of the row's true top-K positions among m sampled ones.
+__device__ __forceinline__ int sample_keep(int K, int m, int n) {
+  const float x = static_cast<float>(K) * static_cast<float>(m) / static_cast<float>(n);
+  return static_cast<int>(ceilf(x + 4.0f * sqrtf(x) + 8.0f));
+}
+
 // ---------------------------------------------------------------------------
-// Fused scorer + streaming exact TopK ("[FlyDSL][DSv4] Prototype FP4 MQA
-// streaming TopK", Changes: scores stream through a bounded LDS pool; each CTA
-// emits only candidate values, indices and a valid count).
-//
-// Each wave owns one query row and its LDS pool of CAP unique keys. A key enters
-// the pool only if it beats the row's gate T (the smallest key that can still be
-// in the row's TopK of this split). When a batch would overflow the pool, the
-// wave radix-selects the K largest keys, drops the rest and raises T.
+// Calibration of the candidate gate ("calibrated candidate filtering", PR 5309
+// Implementation). Per row: exact top-k' of the keys of a sample of its window
+// (every 16th position); the gate is set just below the sample's k'-th key, so
+// that about 16 k' of the window's keys pass it. k' = x + 4 sqrt(x) + 8, where
+// x = K m / n is the expected number of the row's top-K among the m sampled
+// positions, makes "fewer than K keys pass" (underfill) a > 4-sigma event; an
+// underfilled row is still exact, it just takes the fallback. Rows whose sample
+// is not larger than k' get no gate. mode 1 sends every long row to the exact
+// fallback (no prefilter), mode 2 forces an underfill (gate above every key);
+// both exist for testing.
 // ---------------------------------------------------------------------------
-template <int K, int CAP>
-__global__ void __launch_bounds__(kCtaThreads, 1) fused_topk_kernel(ScanArgs a, uint64_t* __restrict__ cand_keys,
-                                                                    int32_t* __restrict__ cand_count) {
-  static_assert(CAP >= K + 64, "pool must hold K keys plus one batch");
+template <int K>
+__global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandArgs c, int mode) {
   __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
-  __shared__ uint64_t s_pool[kRowsPerCta][CAP];
+  __shared__ uint64_t s_pool[kRowsPerCta][kCalCap];
   __shared__ uint32_t s_hist[kRowsPerCta][256];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
@@ -233,127 +370,238 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fused_topk_kernel(ScanArgs a, 
     start = a.row_start[row];
     end = a.row_end[row];
   }
-  int t_begin = 0, t_end = 0;
-  if (!cta_tile_range(a, s_lo, s_hi, active, start, end, wave, lane, &t_begin, &t_end)) return;
+  int u0 = 0, u1 = 0;
+  if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
+  const int base = u0 * kTile;
+  // sampled positions base + 16 j inside this row's window
+  const int j_lo = (start - base + kCalStride - 1) / kCalStride;
+  const int j_hi = (end - base + kCalStride - 1) / kCalStride;
+  const int m = active ? max(0, j_hi - j_lo) : 0;
+  const int kp = active ? sample_keep(K, m, end - start) : 0;
+  const bool gated = mode == 0 && active && kp < m;
 
+  QRow qr;
+  if (gated)
+    load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
+              a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
+              a.weights + static_cast<size_t>(row) * kHeads, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  uint64_t* pool = s_pool[wave];
+  int fill = 0;
+  uint64_t gate = 0;
+  bool bad = false;
+  if (mode == 0) {
+    SampleLoader ld;
+    ld.u0 = u0;
+    const BlockSeq seq{0, (u1 - u0 + kCalStride - 1) / kCalStride};
+    stream_with(ld, a, seq, s_codes, s_scales, [&](int v, const uint8_t* codes, const uint8_t* scales) {
+      if (!gated) return;
+#pragma unroll 1
+      for (int blk = 0; blk < kTile / 64; ++blk) {
+        const int p0 = base + kCalStride * (kTile * v + 64 * blk);     // first position of these 64 samples
+        if (p0 >= end || p0 + kCalStride * 64 <= start) continue;
+        const float sc = score64(qr, codes, scales, blk, lane);
+        const int pos = p0 + kCalStride * lane;
+        const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
+        bool pass = pos >= start && pos < end && key > gate;
+        uint64_t msk = __ballot(pass);
+        if (msk == 0) continue;
+        int cnt = __popcll(msk);
+        if (fill + cnt > kCalCap) {
+          const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
+          if (sel.kept != kp) bad = true;
+          fill = kp;
+          gate = sel.T - 1;
+          pass = pass && key > gate;
+          msk = __ballot(pass);
+          cnt = __popcll(msk);
+        }
+        if (pass) pool[fill + mbcnt64(msk)] = key;
+        fill += cnt;
+      }
+    });
+  }
+  if (!active) return;
+  wave_lds_sync();
+  uint32_t start_count = 0;
+  uint64_t row_gate = 0;
+  if (mode == 1) {
+    start_count = static_cast<uint32_t>(c.cap) + 1;   // overflow marker: exact fallback
+    row_gate = ~0ull;
+  } else if (mode == 2) {
+    row_gate = ~0ull;                                 // nothing passes: underfill
+  } else if (gated) {
+    uint64_t T;
+    if (fill > kp) {
+      const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
+      if (sel.kept != kp) bad = true;
+      T = sel.T;
+    } else {
+      T = wave_min_key(pool, fill, lane);
+    }
+    row_gate = T - 1;
+    if (bad) {                                        // selector failure: exact fallback
+      start_count = static_cast<uint32_t>(c.cap) + 1;
+      row_gate = ~0ull;
+    }
+  }
+  if (lane == 0) {
+    c.count[row] = start_count;
+    c.gate[row] = row_gate;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gated scan: every score block of the split; keys above the row's gate are
+// staged per wave in LDS and appended to the row's candidate buffer (one global
+// atomic per flush). Appends beyond the buffer are dropped but still counted,
+// which the merge detects as an overflow.
+// ---------------------------------------------------------------------------
+template <int K>
+__global__ void __launch_bounds__(kCtaThreads, 2) scan_kernel(ScanArgs a, CandArgs c) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+  __shared__ uint64_t s_stage[kRowsPerCta][kStageCap];
+  __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerCta + wave;
+  bool active = row < a.Q && a.row_state[row] == kRowLong;
+  int start = 0, end = 0;
+  if (active) {
+    start = a.row_start[row];
+    end = a.row_end[row];
+  }
+  int u0 = 0, u1 = 0;
+  if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
+  const BlockSeq seq = split_range(u0, u1, blockIdx.y, a.splits);
+  uint64_t gate = 0;
+  if (active) {
+    gate = c.gate[row];
+    if (c.count[row] > static_cast<uint32_t>(c.cap)) active = false;   // already sent to the fallback
+  }
   QRow qr;
   if (active)
     load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
               a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
               a.weights + static_cast<size_t>(row) * kHeads, lane);
-
-  uint64_t* pool = s_pool[wave];
-  uint32_t* hist = s_hist[wave];
-  int fill = 0;          // wave-uniform
-  uint64_t gate = 0;     // keys > gate may still be in this split's TopK
-  bool failed = false;
-
-  // query operands and weights must be in registers before the scan loop
   __builtin_amdgcn_s_waitcnt(0);
-  TileLoader ld;
-  if (t_begin < t_end) {
-    ld.prologue(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin, t_end, s_codes[t_begin & 1],
-                s_scales[t_begin & 1]);
-    __syncthreads();
-  }
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < t_end;
-    if (more) ld.advance(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t, t_end);
-    const int tb = t * kTile;
-    if (active && tb < end && tb + kTile > start) {
-#pragma unroll 1
-      for (int blk = 0; blk < kTile / 64; ++blk) {
-        const int p0 = tb + 64 * blk;
-        if (p0 >= end || p0 + 64 <= start) continue;
-        const float sc = score64(qr, s_codes[buf], s_scales[buf], blk, lane);
+
+  uint64_t* stage = s_stage[wave];
+  uint64_t* dst = c.cand + static_cast<size_t>(active ? row : 0) * c.cap;
+  int sf = 0;   // staged keys (wave-uniform)
+  auto flush = [&]() {
+    wave_lds_sync();
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&c.count[row], static_cast<uint32_t>(sf));
+    base = __shfl(base, 0, 64);
+    for (int i = lane; i < sf; i += 64) {
+      const uint32_t at = base + static_cast<uint32_t>(i);
+      if (at < static_cast<uint32_t>(c.cap)) dst[at] = stage[i];
+    }
+    wave_lds_sync();
+    sf = 0;
+  };
+  stream_blocks(a, seq, s_codes, s_scales, [&](int t, const uint8_t* codes, const uint8_t* scales) {
+    if (!active) return;
+    for_blocks_in_window(t, start, end, [&](int p0, int blk) {
+      const float sc = score64(qr, codes, scales, blk, lane);
+      const int pos = p0 + lane;
+      const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
+      bool inwin = true;
+      if (p0 < start || p0 + 64 > end) inwin = pos >= start && pos < end;
+      const bool pass = inwin && key > gate;
+      const uint64_t msk = __ballot(pass);
+      if (msk == 0) return;
+      const int cnt = __popcll(msk);
+      if (sf + cnt > kStageCap) flush();
+      if (pass) stage[sf + mbcnt64(msk)] = key;
+      sf += cnt;
+    });
+  });
+  if (active && sf > 0) flush();
+}
+
+// ---------------------------------------------------------------------------
+// Exact streaming TopK without a gate (the fallback of listed rows). Each wave
+// owns one listed row and an LDS pool of CAP unique keys; a key enters only if
+// it beats the pool's gate, and when a batch would overflow the pool the wave
+// radix-selects the K largest, drops the rest and raises the gate. Per (row,
+// fallback split) the top-K keys go to the row's candidate buffer at split * K.
+// Persistent: a fixed grid loops over (8-row chunk of the list, split) items.
+// ---------------------------------------------------------------------------
+template <int K, int CAP, int FBS>
+__global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs a, CandArgs c) {
+  static_assert(CAP >= K + 64, "pool must hold K keys plus one batch");
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+  __shared__ uint64_t s_pool[kRowsPerCta][CAP];
+  __shared__ uint32_t s_hist[kRowsPerCta][256];
+  __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int listed = *c.fb_count;
+  const int chunks = (listed + kRowsPerCta - 1) / kRowsPerCta;
+  for (int item = blockIdx.x; item < chunks * FBS; item += gridDim.x) {
+    const int chunk = item / FBS, split = item % FBS;
+    const int li = chunk * kRowsPerCta + wave;
+    const bool active = li < listed;
+    const int row = active ? c.fb_list[li] : 0;
+    int start = 0, end = 0;
+    if (active) {
+      start = a.row_start[row];
+      end = a.row_end[row];
+    }
+    int u0 = 0, u1 = 0;
+    if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) continue;
+    const BlockSeq seq = split_range(u0, u1, split, FBS);
+    QRow qr;
+    if (active)
+      load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
+                a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
+                a.weights + static_cast<size_t>(row) * kHeads, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    uint64_t* pool = s_pool[wave];
+    uint32_t* hist = s_hist[wave];
+    int fill = 0;
+    uint64_t gate = 0;
+    bool failed = false;
+    stream_blocks(a, seq, s_codes, s_scales, [&](int t, const uint8_t* codes, const uint8_t* scales) {
+      if (!active) return;
+      for_blocks_in_window(t, start, end, [&](int p0, int blk) {
+        const float sc = score64(qr, codes, scales, blk, lane);
         const int pos = p0 + lane;
         const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
         bool pass = pos >= start && pos < end && key > gate;
-        uint64_t m = __ballot(pass);
-        if (m == 0) continue;
-        int cnt = __popcll(m);
+        uint64_t msk = __ballot(pass);
+        if (msk == 0) return;
+        int cnt = __popcll(msk);
         if (fill + cnt > CAP) {
           const Selected sel = wave_select_compact(pool, fill, K, hist, lane);
           if (sel.kept != K) failed = true;
           fill = K;
           gate = sel.T - 1;
           pass = pass && key > gate;
-          m = __ballot(pass);
-          cnt = __popcll(m);
+          msk = __ballot(pass);
+          cnt = __popcll(msk);
         }
-        if (pass) pool[fill + mbcnt64(m)] = key;
+        if (pass) pool[fill + mbcnt64(msk)] = key;
         fill += cnt;
+      });
+    });
+    if (active) {
+      wave_lds_sync();
+      if (fill > K) {
+        const Selected sel = wave_select_compact(pool, fill, K, hist, lane);
+        if (sel.kept != K) failed = true;
+        fill = K;
       }
+      uint64_t* dst = c.cand + static_cast<size_t>(row) * c.cap + static_cast<size_t>(split) * K;
+      for (int i = lane; i < fill; i += 64) dst[i] = pool[i];
+      if (lane == 0) c.fb_cnt[static_cast<size_t>(row) * 4 + split] = failed ? kCodeSelector : fill;
     }
-    if (more) ld.store(s_codes[buf ^ 1], s_scales[buf ^ 1]);
-    __syncthreads();
-  }
-
-  if (!active) return;
-  wave_lds_sync();
-  if (fill > K) {
-    const Selected sel = wave_select_compact(pool, fill, K, hist, lane);
-    if (sel.kept != K) failed = true;
-    fill = K;
-  }
-  const size_t slot = static_cast<size_t>(row) * a.splits + blockIdx.y;
-  uint64_t* dst = cand_keys + slot * K;
-  for (int i = lane; i < fill; i += 64) dst[i] = pool[i];
-  if (lane == 0) cand_count[slot] = failed ? kCodeSelector : fill;
-}
-
-// ---------------------------------------------------------------------------
-// Dense scorer (comparator): same streaming and the same score64() as the fused
-// kernel, but every score inside an active row's window goes to logits[row, s].
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kCtaThreads, 1) dense_score_kernel(ScanArgs a, float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
-  __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerCta + wave;
-  const bool active = row < a.Q && a.row_state[row] == kRowLong;
-  int start = 0, end = 0;
-  if (active) {
-    start = a.row_start[row];
-    end = a.row_end[row];
-  }
-  int t_begin = 0, t_end = 0;
-  if (!cta_tile_range(a, s_lo, s_hi, active, start, end, wave, lane, &t_begin, &t_end)) return;
-  QRow qr;
-  if (active)
-    load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
-              a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
-              a.weights + static_cast<size_t>(row) * kHeads, lane);
-  float* out = logits + static_cast<size_t>(row) * (a.P_log * kPage);
-
-  // query operands and weights must be in registers before the scan loop
-  __builtin_amdgcn_s_waitcnt(0);
-  TileLoader ld;
-  if (t_begin < t_end) {
-    ld.prologue(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t_begin, t_end, s_codes[t_begin & 1],
-                s_scales[t_begin & 1]);
-    __syncthreads();
-  }
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < t_end;
-    if (more) ld.advance(a.k_pages, a.k_scale, a.page_table, a.P_log, a.P_phys, t, t_end);
-    const int tb = t * kTile;
-    if (active && tb < end && tb + kTile > start) {
-#pragma unroll 1
-      for (int blk = 0; blk < kTile / 64; ++blk) {
-        const int p0 = tb + 64 * blk;
-        if (p0 >= end || p0 + 64 <= start) continue;
-        const float sc = score64(qr, s_codes[buf], s_scales[buf], blk, lane);
-        const int pos = p0 + lane;
-        if (pos >= start && pos < end) __builtin_nontemporal_store(sc, out + pos);
-      }
-    }
-    if (more) ld.store(s_codes[buf ^ 1], s_scales[buf ^ 1]);
-    __syncthreads();
+    __syncthreads();   // LDS pools and block buffers are reused by the next item
   }
 }
 
@@ -556,63 +804,46 @@ __device__ __forceinline__ void fail_row(int64_t row, int code, int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Exact merge of the split candidates ("exact candidate union", PR 5282) +
-// page mapping + emission. One 256-thread CTA per long row.
+// Exact merge of the gated candidates + page mapping + emission. One 256-thread
+// CTA per long row. The candidates are all of the window's keys above the gate;
+// with at least K of them the row's top-K is among them ("exact candidate
+// union", PR 5282). Otherwise (or on overflow) the row is listed for the exact
+// fallback and its outputs are written there.
 // ---------------------------------------------------------------------------
 template <int K>
-__global__ void __launch_bounds__(256) merge_emit_kernel(
-    const int32_t* __restrict__ row_state, const uint64_t* __restrict__ cand_keys,
-    const int32_t* __restrict__ cand_count, int32_t splits, const int32_t* __restrict__ page_table,
-    int64_t P_log, int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot,
-    int32_t* __restrict__ out_count, float* __restrict__ out_score) {
+__global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ row_state, CandArgs c,
+                                                    const int32_t* __restrict__ page_table, int64_t P_log,
+                                                    int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot,
+                                                    int32_t* __restrict__ out_count, float* __restrict__ out_score) {
   constexpr int NT = 256;
   __shared__ uint64_t s_sel[K];
   __shared__ uint32_t s_hist[256];
-  __shared__ int32_t s_cnt[256];
-  __shared__ int32_t s_off[257];
   __shared__ BlockScratch<NT> s_red;
   __shared__ int32_t s_n;
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
-  const uint64_t* keys = cand_keys + static_cast<size_t>(row) * splits * K;
-  for (int i = threadIdx.x; i < splits; i += NT) s_cnt[i] = cand_count[static_cast<size_t>(row) * splits + i];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0, bad = 0;
-    for (int i = 0; i < splits; ++i) {
-      s_off[i] = acc;
-      if (s_cnt[i] < 0 || s_cnt[i] > K) bad = 1;
-      else acc += s_cnt[i];
-    }
-    s_off[splits] = bad ? -1 : acc;
-  }
-  __syncthreads();
-  const int total = s_off[splits];
-  if (total < K) {   // a long row always has >= K candidates
-    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+  const uint32_t n = c.count[row];
+  if (n > static_cast<uint32_t>(c.cap) || n < static_cast<uint32_t>(K)) {
+    if (threadIdx.x == 0) c.fb_list[atomicAdd(c.fb_count, 1)] = static_cast<int32_t>(row);
     return;
   }
-  if (total == K) {
-    for (int e = threadIdx.x; e < splits * K; e += NT) {
-      const int sp = e / K, j = e % K;
-      if (j < s_cnt[sp]) s_sel[s_off[sp] + j] = keys[e];
-    }
+  const uint64_t* keys = c.cand + static_cast<size_t>(row) * c.cap;
+  if (n == static_cast<uint32_t>(K)) {
+    for (int i = threadIdx.x; i < K; i += NT) s_sel[i] = keys[i];
     __syncthreads();
   } else {
-    auto src = [&](int64_t e, uint64_t& x) -> bool {
-      const int sp = static_cast<int>(e / K), j = static_cast<int>(e % K);
-      if (j >= s_cnt[sp]) return false;
-      x = keys[e];
+    auto src = [&](int64_t i, uint64_t& x) -> bool {
+      x = keys[i];
       return true;
     };
     bool ok = false;
-    const uint64_t T = block_radix_select<NT, 8>(src, static_cast<int64_t>(splits) * K, K, s_hist, s_red, &ok);
+    const uint64_t T = block_radix_select<NT, 8>(src, static_cast<int64_t>(n), K, s_hist, s_red, &ok);
     if (threadIdx.x == 0) s_n = 0;
     __syncthreads();
     if (ok) {
-      for (int e = threadIdx.x; e < splits * K; e += NT) {
-        uint64_t x;
-        if (src(e, x) && x >= T) {
+      for (int i = threadIdx.x; i < static_cast<int>(n); i += NT) {
+        const uint64_t x = keys[i];
+        if (x >= T) {
           const int at = atomicAdd(&s_n, 1);
           if (at < K) s_sel[at] = x;
         }
@@ -625,6 +856,107 @@ __global__ void __launch_bounds__(256) merge_emit_kernel(
     }
   }
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
+}
+
+// Exact merge of the fallback's per-split top-K keys of each listed row.
+// Persistent over the list. A listed row always has >= K candidates (it is
+// longer than K); fewer means a selector failure and fails the row closed.
+template <int K, int FBS>
+__global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const int32_t* __restrict__ page_table,
+                                                             int64_t P_log, int32_t* __restrict__ out_raw,
+                                                             int32_t* __restrict__ out_slot,
+                                                             int32_t* __restrict__ out_count,
+                                                             float* __restrict__ out_score) {
+  constexpr int NT = 256;
+  __shared__ uint64_t s_sel[K];
+  __shared__ uint32_t s_hist[256];
+  __shared__ int32_t s_cnt[FBS];
+  __shared__ BlockScratch<NT> s_red;
+  __shared__ int32_t s_n, s_total;
+  const int listed = *c.fb_count;
+  for (int li = blockIdx.x; li < listed; li += gridDim.x) {
+    const int64_t row = c.fb_list[li];
+    const uint64_t* keys = c.cand + static_cast<size_t>(row) * c.cap;
+    if (threadIdx.x == 0) {
+      int total = 0;
+      for (int i = 0; i < FBS; ++i) {
+        s_cnt[i] = c.fb_cnt[static_cast<size_t>(row) * 4 + i];
+        if (s_cnt[i] < 0 || s_cnt[i] > K) total = -1000000;
+        total += s_cnt[i];
+      }
+      s_total = total;
+      s_n = 0;
+    }
+    __syncthreads();
+    if (s_total < K) {
+      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+      __syncthreads();
+      continue;
+    }
+    auto src = [&](int64_t e, uint64_t& x) -> bool {
+      const int sp = static_cast<int>(e / K), j = static_cast<int>(e % K);
+      if (j >= s_cnt[sp]) return false;
+      x = keys[e];
+      return true;
+    };
+    bool ok = true;
+    uint64_t T = 0;
+    if (s_total > K) T = block_radix_select<NT, 8>(src, static_cast<int64_t>(FBS) * K, K, s_hist, s_red, &ok);
+    if (ok) {
+      for (int e = threadIdx.x; e < FBS * K; e += NT) {
+        uint64_t x;
+        if (src(e, x) && x >= T) {
+          const int at = atomicAdd(&s_n, 1);
+          if (at < K) s_sel[at] = x;
+        }
+      }
+    }
+    __syncthreads();
+    if (!ok || s_n != K) {
+      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+    } else {
+      emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense scorer (comparator): same streaming and the same score64() as the
+// fused path, but every score inside an active row's window goes to
+// logits[row, s].
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kCtaThreads, 2) dense_score_kernel(ScanArgs a, float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+  __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerCta + wave;
+  const bool active = row < a.Q && a.row_state[row] == kRowLong;
+  int start = 0, end = 0;
+  if (active) {
+    start = a.row_start[row];
+    end = a.row_end[row];
+  }
+  int u0 = 0, u1 = 0;
+  if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
+  QRow qr;
+  if (active)
+    load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
+              a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
+              a.weights + static_cast<size_t>(row) * kHeads, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  float* out = logits + static_cast<size_t>(active ? row : 0) * (a.P_log * kPage);
+  stream_blocks(a, split_range(u0, u1, blockIdx.y, a.splits), s_codes, s_scales,
+                [&](int t, const uint8_t* codes, const uint8_t* scales) {
+                  if (!active) return;
+                  for_blocks_in_window(t, start, end, [&](int p0, int blk) {
+                    const float sc = score64(qr, codes, scales, blk, lane);
+                    const int pos = p0 + lane;
+                    if (pos >= start && pos < end) __builtin_nontemporal_store(sc, out + pos);
+                  });
+                });
 }
 
 // ---------------------------------------------------------------------------
@@ -672,9 +1004,26 @@ __global__ void __launch_bounds__(1024) logits_topk_kernel(
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
 }
 
-// Pool capacity per row: all LDS left after the two score-block buffers and the
-// per-wave histograms (160 KiB per CTA on gfx950).
+// Gated candidate buffer per row, and the fallback's pool and splits.
+template <int K>
+struct Geometry;
+template <>
+struct Geometry<512> {
+  static constexpr int kCap = 2048;
+  static constexpr int kFbSplits = 4;
+};
+template <>
+struct Geometry<1024> {
+  static constexpr int kCap = 2560;
+  static constexpr int kFbSplits = 2;
+};
+// Fallback pool per row: all LDS left after the block buffers and histograms.
 constexpr int kPoolCap = 1856;
+constexpr int kFallbackGrid = 256;
+static_assert(Geometry<512>::kFbSplits * 512 <= Geometry<512>::kCap, "fallback keys fit the candidate buffer");
+static_assert(Geometry<1024>::kFbSplits * 1024 <= Geometry<1024>::kCap, "fallback keys fit the candidate buffer");
+
+int candidate_cap(int K) { return K == 512 ? Geometry<512>::kCap : Geometry<1024>::kCap; }
 
 // ---------------------------------------------------------------------------
 // Launchers
@@ -697,37 +1046,60 @@ static ScanArgs scan_args(const PathArgs& p, const int32_t* row_state, int32_t s
   return a;
 }
 
-hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, hipStream_t st) {
+static CandArgs cand_args(const GatedScratch& g, int K) {
+  CandArgs c;
+  c.gate = g.gate;
+  c.count = g.count;
+  c.cand = g.cand;
+  c.fb_list = g.fb_list;
+  c.fb_count = g.fb_count;
+  c.fb_cnt = g.fb_cnt;
+  c.cap = candidate_cap(K);
+  return c;
+}
+
+hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int32_t* fb_count, hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
   row_prep_kernel<<<dim3(static_cast<unsigned>(p.Q)), dim3(256), 0, st>>>(
       p.row_start, p.row_end, p.page_table, p.P_log, p.P_phys, p.K, mode, p.out_raw, p.out_slot,
-      p.out_count, p.out_score, row_state);
+      p.out_count, p.out_score, row_state, fb_count);
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const PathArgs& p, const int32_t* row_state, int32_t splits, uint64_t* cand_keys,
-                        int32_t* cand_count, hipStream_t st) {
-  if (p.Q == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta), static_cast<unsigned>(splits));
-  const ScanArgs a = scan_args(p, row_state, splits);
-  if (p.K == 512)
-    fused_topk_kernel<512, kPoolCap><<<grid, dim3(kCtaThreads), 0, st>>>(a, cand_keys, cand_count);
-  else
-    fused_topk_kernel<1024, kPoolCap><<<grid, dim3(kCtaThreads), 0, st>>>(a, cand_keys, cand_count);
+template <int K>
+static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
+                                 int stage, hipStream_t st) {
+  using G = Geometry<K>;
+  const ScanArgs a = scan_args(p, g.row_state, splits);
+  const CandArgs c = cand_args(g, K);
+  const unsigned tiles = static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta);
+  switch (stage) {
+    case 0:
+      calib_kernel<K><<<dim3(tiles), dim3(kCtaThreads), 0, st>>>(a, c, calib_mode);
+      break;
+    case 1:
+      scan_kernel<K><<<dim3(tiles, static_cast<unsigned>(splits)), dim3(kCtaThreads), 0, st>>>(a, c);
+      break;
+    case 2:
+      merge_kernel<K><<<dim3(static_cast<unsigned>(p.Q)), dim3(256), 0, st>>>(
+          g.row_state, c, p.page_table, p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
+      break;
+    case 3:
+      fallback_scan_kernel<K, kPoolCap, G::kFbSplits><<<dim3(kFallbackGrid), dim3(kCtaThreads), 0, st>>>(a, c);
+      break;
+    default:
+      fallback_merge_kernel<K, G::kFbSplits><<<dim3(kFallbackGrid), dim3(256), 0, st>>>(
+          c, p.page_table, p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
+      break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const PathArgs& p, const int32_t* row_state, int32_t splits, const uint64_t* cand_keys,
-                        const int32_t* cand_count, hipStream_t st) {
+hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode, int stage,
+                              hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(p.Q));
-  if (p.K == 512)
-    merge_emit_kernel<512><<<grid, dim3(256), 0, st>>>(row_state, cand_keys, cand_count, splits, p.page_table,
-                                                        p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
-  else
-    merge_emit_kernel<1024><<<grid, dim3(256), 0, st>>>(row_state, cand_keys, cand_count, splits, p.page_table,
-                                                         p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
-  return hipGetLastError();
+  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_mode, stage, st)
+                    : launch_gated_k<1024>(p, g, splits, calib_mode, stage, st);
 }
 
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
@@ -765,7 +1137,5 @@ hipError_t status_take(hipStream_t st, int32_t* host_out) {
   if (e != hipSuccess) return e;
   return hipStreamSynchronize(st);
 }
-
-int pool_capacity() { return kPoolCap; }
 
 }  // namespace mqa

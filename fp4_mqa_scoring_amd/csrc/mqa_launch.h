@@ -26,18 +26,33 @@ struct PathArgs {
   float* out_score;
 };
 
+// Scratch of the gated fused path (one call).
+struct GatedScratch {
+  int32_t* row_state;   // [Q]
+  uint64_t* gate;       // [Q]
+  uint32_t* count;      // [Q]
+  int32_t* fb_list;     // [Q]
+  int32_t* fb_count;    // [1]
+  int32_t* fb_cnt;      // [Q, 4]
+  uint64_t* cand;       // [Q, candidate_cap(K)]
+};
+
+// Candidate keys kept per row by the gated path.
+int candidate_cap(int K);
+
 // mode 0: TopK (answers short and invalid rows); mode 1: logits only.
-hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, hipStream_t st);
-hipError_t launch_fused(const PathArgs& p, const int32_t* row_state, int32_t splits, uint64_t* cand_keys,
-                        int32_t* cand_count, hipStream_t st);
-hipError_t launch_merge(const PathArgs& p, const int32_t* row_state, int32_t splits, const uint64_t* cand_keys,
-                        const int32_t* cand_count, hipStream_t st);
+// fb_count (nullable) is cleared for the gated path.
+hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int32_t* fb_count, hipStream_t st);
+// Stages of the gated fused path: 0 calibration (calib_mode 0 normal, 1 no
+// prefilter, 2 forced underfill), 1 gated scan, 2 merge, 3 fallback scan,
+// 4 fallback merge.
+hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode, int stage,
+                              hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
                               hipStream_t st);
 hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int32_t* row_state,
                               hipStream_t st);
 // Copies the sticky status word to *host_out and clears it (synchronises st).
 hipError_t status_take(hipStream_t st, int32_t* host_out);
-int pool_capacity();
 
 }  // namespace mqa

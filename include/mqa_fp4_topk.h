@@ -92,6 +92,10 @@ extern "C" {
 
 /* ---- flags of the _ex entry point -------------------------------------------- */
 #define MQA_FLAG_SPLITS_MASK 0xFFu   /* context splits per row tile, 0 = automatic (1..255) */
+#define MQA_FLAG_NO_PREFILTER 0x100u /* no calibrated candidate gate: every long row takes the
+                                        exact ungated streaming path */
+#define MQA_FLAG_FORCE_UNDERFILL 0x200u /* gate above every key, so every long row underfills
+                                           and takes the fallback (for tests) */
 
 /*
  * Fused FP4 scoring + exact TopK + page mapping (the hot path).

@@ -63,7 +63,8 @@ def test_unsupported_k_rejected_before_any_device_work(lib, K):
 
 
 def test_bad_flags_sizes_nulls_alignment_rejected_on_host(lib):
-    assert _call_prefill(lib, flags=0x100) == -8
+    assert _call_prefill(lib, flags=0x400) == -8
+    assert _call_prefill(lib, flags=0x300) == -8                # no prefilter + forced underfill
     assert _call_prefill(lib, Q=-1) == -4
     assert _call_prefill(lib, P_log=(1 << 31) // 64) == -4
     assert _call_prefill(lib, P_phys=(1 << 31) // 64 + 1) == -4

@@ -144,6 +144,43 @@ def test_splits_do_not_change_outputs(K):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"splits={splits}"
 
 
+@pytest.mark.parametrize("K", [512, 1024])
+def test_prefilter_off_and_forced_underfill_give_identical_outputs(K):
+    """The calibrated gate is a pure speed-up: without it (every long row on the
+    exact ungated path) and with a gate above every key (every long row
+    underfills and falls back) the outputs are bit-identical."""
+    _need_gpu()
+    inp = medium_inputs(seed=13 + K, K=K, S=4096 if K == 1024 else 2560)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K)
+    check_rows(inp, range(inp.Q), base[0], base[1], base[2], base[3], where=f"gated K={K}")
+    for flags in (mqa.FLAG_NO_PREFILTER, mqa.FLAG_FORCE_UNDERFILL, mqa.FLAG_NO_PREFILTER | 3,
+                  mqa.FLAG_FORCE_UNDERFILL | 5):
+        got = gu.run_fused(dev, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+    assert mqa.mqa_fp4_status() == 0
+
+
+def test_long_windows_use_the_gate_and_match_the_oracle():
+    """Windows long enough for a calibrated gate (many sampled score blocks),
+    with ties and duplicates, across several splits."""
+    _need_gpu()
+    Q, S, K = 24, 64 * 640, 1024
+    rng = np.random.default_rng(99)
+    st = rng.integers(0, 3000, Q).astype(np.int32)
+    en = np.minimum(st + rng.integers(20000, S, Q), S).astype(np.int32)
+    inp = synth.make_inputs(Q, S, K, 1234, row_start=st, row_end=en, dup_frac=0.2)
+    inp.q[5] = 0                                            # all-equal scores
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K)
+    check_rows(inp, range(Q), base[0], base[1], base[2], base[3], where="gated long")
+    for flags in (1, 4, 16, mqa.FLAG_NO_PREFILTER):
+        got = gu.run_fused(dev, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+
+
 def test_non_default_stream_gives_same_outputs():
     _need_gpu()
     import torch
