@@ -35,8 +35,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_bits(float s) {
   const uint32_t b = __float_as_uint(s);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0u;        // every NaN: lowest class
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);     // negatives (and -0) flipped
+  // non-negative (sign 0): set the top bit; negative (and -0): flip all bits
+  const uint32_t o = b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
+  return __builtin_isnan(s) ? 0u : o;                    // every NaN: lowest class
 }
 
 __device__ __forceinline__ uint64_t make_key(float s, uint32_t pos) {
@@ -200,6 +201,77 @@ __device__ __forceinline__ float score64(const QRow& r, const uint8_t* s_codes,
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
                                                    __float_as_uint(part[1]), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined scoring of one 256-position score block for one row.
+// The 8 groups of 32 positions are processed so that the MFMAs of group g+1 are
+// issued before the ReLU + head-weighted epilogue of group g, letting the
+// matrix core and the VALU work at the same time within one wave. The swizzled
+// LDS chunk offsets depend only on lane % 32, so every B-operand address is a
+// per-lane base plus a compile-time offset. Same arithmetic, in the same order,
+// as score64(): the scores are bit-identical.
+// emit(blk, score) is called for blk = 0..3 with lane l holding position
+// 64*blk + l of the block.
+// ---------------------------------------------------------------------------
+struct LaneOffsets {
+  int code0, code1, scale;
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
+  const int r = lane & 31, g = lane >> 5;
+  const int sw = chunk_swizzle(r);   // equal to chunk_swizzle(32 * grp + r) for every grp
+  return LaneOffsets{r * kVecBytes + 16 * ((2 * g) ^ sw), r * kVecBytes + 16 * ((2 * g + 1) ^ sw),
+                     r * kVecScales + 2 * g};
+}
+
+struct GroupAcc {
+  v16f d0, d1;
+};
+
+template <int GRP>
+__device__ __forceinline__ GroupAcc mfma_group(const QRow& r, const uint8_t* s_codes, const uint8_t* s_scales,
+                                               const LaneOffsets& o) {
+  const v4i b0 = *reinterpret_cast<const v4i*>(s_codes + o.code0 + GRP * 32 * kVecBytes);
+  const v4i b1 = *reinterpret_cast<const v4i*>(s_codes + o.code1 + GRP * 32 * kVecBytes);
+  const int ks = *reinterpret_cast<const uint16_t*>(s_scales + o.scale + GRP * 32 * kVecScales);
+  const v16f z = {};
+  GroupAcc acc;
+  acc.d0 = mfma_fp4<0, 0>(r.a[0][0], b0, z, r.scale, ks);
+  acc.d0 = mfma_fp4<1, 1>(r.a[0][1], b1, acc.d0, r.scale, ks);
+  acc.d1 = mfma_fp4<2, 0>(r.a[1][0], b0, z, r.scale, ks);
+  acc.d1 = mfma_fp4<3, 1>(r.a[1][1], b1, acc.d1, r.scale, ks);
+  return acc;
+}
+
+template <class Emit>
+__device__ __forceinline__ void score_block_pipelined(const QRow& r, const uint8_t* s_codes,
+                                                      const uint8_t* s_scales, const LaneOffsets& o,
+                                                      Emit&& emit) {
+  GroupAcc a0 = mfma_group<0>(r, s_codes, s_scales, o);
+  GroupAcc a1 = mfma_group<1>(r, s_codes, s_scales, o);
+  float p0 = head_partial(r, a0.d0, a0.d1);
+  a0 = mfma_group<2>(r, s_codes, s_scales, o);
+  float p1 = head_partial(r, a1.d0, a1.d1);
+  a1 = mfma_group<3>(r, s_codes, s_scales, o);
+  auto combine = [](float x, float y) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  };
+  emit(0, combine(p0, p1));
+  p0 = head_partial(r, a0.d0, a0.d1);
+  a0 = mfma_group<4>(r, s_codes, s_scales, o);
+  p1 = head_partial(r, a1.d0, a1.d1);
+  a1 = mfma_group<5>(r, s_codes, s_scales, o);
+  emit(1, combine(p0, p1));
+  p0 = head_partial(r, a0.d0, a0.d1);
+  a0 = mfma_group<6>(r, s_codes, s_scales, o);
+  p1 = head_partial(r, a1.d0, a1.d1);
+  a1 = mfma_group<7>(r, s_codes, s_scales, o);
+  emit(2, combine(p0, p1));
+  p0 = head_partial(r, a0.d0, a0.d1);
+  p1 = head_partial(r, a1.d0, a1.d1);
+  emit(3, combine(p0, p1));
 }
 
 // ---------------------------------------------------------------------------

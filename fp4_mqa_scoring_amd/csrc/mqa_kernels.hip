@@ -21,8 +21,8 @@
 // logits [Q, S]) + logits_topk.
 //
 // Sources: "[FlyDSL] Add FP4 LiteTopK prefill operator" (ROCm/aiter PR 5309),
-// Implementation (calibrated candidate filtering, stable exact TopK, page
-// mapping, fail closed); "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
+// Implementation (a calibrated filter of candidates, exact and stable selection,
+// the page map, failing closed); "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
 // (ROCm/aiter PR 5282), Changes and Scope.
 #include "mqa_device.h"
 #include "mqa_launch.h"
@@ -503,15 +503,17 @@ __global__ void __launch_bounds__(kCtaThreads, 2) scan_kernel(ScanArgs a, CandAr
     wave_lds_sync();
     sf = 0;
   };
+  const LaneOffsets lo = lane_offsets(lane);
   stream_blocks(a, seq, s_codes, s_scales, [&](int t, const uint8_t* codes, const uint8_t* scales) {
     if (!active) return;
-    for_blocks_in_window(t, start, end, [&](int p0, int blk) {
-      const float sc = score64(qr, codes, scales, blk, lane);
-      const int pos = p0 + lane;
+    const int tb = t * kTile;
+    if (tb >= end || tb + kTile <= start) return;
+    const bool inside = tb >= start && tb + kTile <= end;   // no window mask needed
+    score_block_pipelined(qr, codes, scales, lo, [&](int blk, float sc) {
+      const int pos = tb + 64 * blk + lane;
       const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
-      bool inwin = true;
-      if (p0 < start || p0 + 64 > end) inwin = pos >= start && pos < end;
-      const bool pass = inwin && key > gate;
+      bool pass = key > gate;
+      if (!inside) pass = pass && pos >= start && pos < end;
       const uint64_t msk = __ballot(pass);
       if (msk == 0) return;
       const int cnt = __popcll(msk);

@@ -8,10 +8,12 @@ Workload shapes follow the pages:
 - "[FlyDSL] Add FP4 LiteTopK prefill operator" (ROCm/aiter PR 5309), Summary,
   model table: Q=8192 rows, H=64 heads, D=128, K=512 (V4-Flash) or 1024
   (V4-Pro), C4 context = raw / 4; Validation table: C4 widths 65,536,
-  131,072 and 196,608 ("deterministic tensors with the released model shapes").
+  131,072 and 196,608; the pages benchmark fixed synthetic tensors shaped like
+  the released models.
 - "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK" (ROCm/aiter PR 5282),
-  Scope: page size 64, score block 256, ragged prefill windows, shuffled page
-  tables; runtime update: rows=1024 production grid at C4 196,608 / 262,144.
+  Scope: 64-position KV pages, 256-position score blocks, ragged prefill
+  windows, shuffled page tables; runtime update: 1024-row production grid at
+  C4 widths 196,608 and 262,144.
 
 Layout of one input set (all numpy, C-contiguous):
   q          uint8   [Q, 64, 64]   E2M1 codes, two per byte; element 2j is the

@@ -33,9 +33,9 @@
  *   weights    float  [Q, 64]
  *   page_table int32  [P_log]            logical page -> physical page; S = 64 * P_log
  *   row_start, row_end int32 [Q]         window [start, end) in logical C4 positions
- *   out_raw, out_slot  int32 [Q, K]      written in place (PR 38101 of sglang, Changes:
- *                                        "write final physical C4 slots and optional
- *                                        raw indices in place")
+ *   out_raw, out_slot  int32 [Q, K]      filled in place by the library (sglang PR 38101,
+ *                                        Changes: slots and, optionally, raw
+ *                                        positions go straight into caller buffers)
  *   out_count  int32  [Q]                min(len, K), or a negative per-row code
  *   out_score  float  [Q, K] (optional)  fp32 score of each selected position;
  *                                        NaN for padding and for short rows
@@ -52,8 +52,8 @@
  * ownership, 64-bit addressing). Work is enqueued on `stream` (a hipStream_t;
  * NULL = the legacy default stream of the current device), which must belong to
  * the device the tensors live on; the caller's current device is restored
- * before returning. The success path never synchronises. Graph capture is
- * rejected (PR 5282, Scope: graph capture is rejected explicitly in this first
+ * before returning. The success path never synchronises. A capturing stream is
+ * refused with MQA_ERR_CAPTURING (PR 5282, Scope: no graph capture in the first
  * version). Calls on the same stream are ordered; calls on different streams
  * use separate stream-ordered scratch and may run concurrently.
  */
@@ -125,8 +125,8 @@ int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_
 
 /*
  * Dense comparator (the legacy full-logits path the pages measure against:
- * PR 5282 Motivation, "materializes an FP32 [query_rows, c4_context] score
- * matrix before TopK"). Writes the fp32 score of every position inside each
+ * PR 5282 Motivation, where the whole fp32 row-by-context score matrix is built
+ * first and TopK runs on it afterwards). Writes the fp32 score of every position inside each
  * long row's window (length > K) into logits[q * 64 * P_log + s] (caller-owned
  * [Q, S] buffer; entries outside those windows are left untouched), then selects
  * exactly as mqa_fp4_topk_prefill. Scores are bit-identical to the fused path.

@@ -210,7 +210,8 @@ int64_t oracle_select_topk(const double* scores, int64_t n, int64_t start, int64
 }
 
 /* Physical slot of a raw logical position: page_table[raw / 64] * 64 + raw % 64;
- * -1 stays -1 ([P2] Changes: map raw C4 positions through the page table). */
+ * -1 stays -1 ([P2] Changes: logical positions are translated into physical slots by the
+ * page table). */
 int64_t oracle_slot(int64_t raw, const int32_t* page_table) {
     if (raw < 0) return -1;
     return (int64_t)page_table[raw / ORACLE_PAGE] * ORACLE_PAGE + raw % ORACLE_PAGE;
