@@ -167,7 +167,9 @@ __device__ __forceinline__ float relu_bits(float x) {
 }
 
 // Partial indexer score of the 32 heads this lane holds for its position:
-// sum over (hb, v) in a fixed order, starting at +0.
+// sum over (hb, v) in a fixed order, starting at +0. One dependent chain: with
+// four waves per SIMD the FMA latency is hidden by the other waves, and extra
+// accumulators only add instructions.
 __device__ __forceinline__ float head_partial(const QRow& r, const v16f& d0, const v16f& d1) {
   float p = 0.0f;
 #pragma unroll
@@ -204,13 +206,14 @@ __device__ __forceinline__ float score64(const QRow& r, const uint8_t* s_codes,
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined scoring of one 256-position score block for one row.
-// The 8 groups of 32 positions are processed so that the MFMAs of group g+1 are
-// issued before the ReLU + head-weighted epilogue of group g, letting the
-// matrix core and the VALU work at the same time within one wave. The swizzled
-// LDS chunk offsets depend only on lane % 32, so every B-operand address is a
-// per-lane base plus a compile-time offset. Same arithmetic, in the same order,
-// as score64(): the scores are bit-identical.
+// Scoring of one 256-position score block for one row, as 8 groups of 32
+// positions (4 MFMAs each, then the ReLU + head-weighted epilogue). On gfx950 a
+// SIMD does not run MFMA and VALU work at the same time, so there is nothing to
+// gain from keeping two groups in flight inside a wave; the register budget goes
+// to occupancy instead (four waves per SIMD hide the MFMA and LDS latencies).
+// The swizzled LDS chunk offsets depend only on lane % 32, so every B-operand
+// address is a per-lane base plus a compile-time offset. Same arithmetic, in the
+// same order, as score64(): the scores are bit-identical.
 // emit(blk, score) is called for blk = 0..3 with lane l holding position
 // 64*blk + l of the block.
 // ---------------------------------------------------------------------------
@@ -244,34 +247,33 @@ __device__ __forceinline__ GroupAcc mfma_group(const QRow& r, const uint8_t* s_c
   return acc;
 }
 
+// Lanes l and l+32 hold complementary heads of one position; swapping halves
+// gives lane l < 32 position l of group x and lane l >= 32 position l of group y.
+__device__ __forceinline__ float combine_halves(float x, float y) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+template <int G, class Emit>
+__device__ __forceinline__ void score_groups(const QRow& r, const uint8_t* s_codes, const uint8_t* s_scales,
+                                             const LaneOffsets& o, float& even, Emit& emit) {
+  if constexpr (G < 8) {
+    const GroupAcc a = mfma_group<G>(r, s_codes, s_scales, o);
+    const float p = head_partial(r, a.d0, a.d1);
+    if constexpr (G % 2 == 0) {
+      even = p;
+    } else {
+      emit(G / 2, combine_halves(even, p));
+    }
+    score_groups<G + 1>(r, s_codes, s_scales, o, even, emit);
+  }
+}
+
 template <class Emit>
-__device__ __forceinline__ void score_block_pipelined(const QRow& r, const uint8_t* s_codes,
-                                                      const uint8_t* s_scales, const LaneOffsets& o,
-                                                      Emit&& emit) {
-  GroupAcc a0 = mfma_group<0>(r, s_codes, s_scales, o);
-  GroupAcc a1 = mfma_group<1>(r, s_codes, s_scales, o);
-  float p0 = head_partial(r, a0.d0, a0.d1);
-  a0 = mfma_group<2>(r, s_codes, s_scales, o);
-  float p1 = head_partial(r, a1.d0, a1.d1);
-  a1 = mfma_group<3>(r, s_codes, s_scales, o);
-  auto combine = [](float x, float y) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  };
-  emit(0, combine(p0, p1));
-  p0 = head_partial(r, a0.d0, a0.d1);
-  a0 = mfma_group<4>(r, s_codes, s_scales, o);
-  p1 = head_partial(r, a1.d0, a1.d1);
-  a1 = mfma_group<5>(r, s_codes, s_scales, o);
-  emit(1, combine(p0, p1));
-  p0 = head_partial(r, a0.d0, a0.d1);
-  a0 = mfma_group<6>(r, s_codes, s_scales, o);
-  p1 = head_partial(r, a1.d0, a1.d1);
-  a1 = mfma_group<7>(r, s_codes, s_scales, o);
-  emit(2, combine(p0, p1));
-  p0 = head_partial(r, a0.d0, a0.d1);
-  p1 = head_partial(r, a1.d0, a1.d1);
-  emit(3, combine(p0, p1));
+__device__ __forceinline__ void score_block(const QRow& r, const uint8_t* s_codes, const uint8_t* s_scales,
+                                            const LaneOffsets& o, Emit&& emit) {
+  float even = 0.0f;
+  score_groups<0>(r, s_codes, s_scales, o, even, emit);
 }
 
 // ---------------------------------------------------------------------------

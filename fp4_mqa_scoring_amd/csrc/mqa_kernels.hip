@@ -91,70 +91,8 @@ __global__ void __launch_bounds__(256) row_prep_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Score-block streaming shared by all scoring kernels. One CTA = 8 query rows
-// (one per wave) x a sequence of 256-position score blocks. Each block (4 pages
-// = 16 KiB codes + 1 KiB scales) is gathered through the page table with
-// coalesced 32-byte-per-thread loads into registers one block ahead (page-table
-// entries two blocks ahead), then written to a double-buffered LDS image.
-// ---------------------------------------------------------------------------
-struct TileLoader {
-  v4i c0, c1, sc;
-  int32_t code_entry, scale_entry;   // raw page-table entries fetched ahead
-  int64_t code_page, scale_page;     // validated physical pages of the block to load next
-
-  __device__ __forceinline__ static int64_t valid_or_neg(int32_t e, int64_t P_phys) {
-    return (e >= 0 && e < P_phys) ? e : -1;
-  }
-
-  // Page-table entries of score block t for this thread's code chunk and (first
-  // wave) scale chunk; -1 beyond the table.
-  __device__ __forceinline__ void fetch_entries(const int32_t* pt, int64_t P_log, int t) {
-    const int tid = threadIdx.x;
-    const int64_t lp = static_cast<int64_t>(t) * kTilePages + (tid >> 7);
-    code_entry = lp < P_log ? pt[lp] : -1;
-    const int64_t slp = static_cast<int64_t>(t) * kTilePages + ((tid & 63) >> 4);
-    scale_entry = slp < P_log ? pt[slp] : -1;
-  }
-
-  __device__ __forceinline__ void resolve(int64_t P_phys) {
-    code_page = valid_or_neg(code_entry, P_phys);
-    scale_page = valid_or_neg(scale_entry, P_phys);
-  }
-
-  // Global -> registers for the resolved score block. Pages with an
-  // out-of-range entry are not read (their rows were rejected by row_prep).
-  __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale) {
-    const int tid = threadIdx.x;
-    const int within = tid & 127;
-    if (code_page >= 0) {
-      const v4i* src = reinterpret_cast<const v4i*>(k_pages + static_cast<size_t>(code_page) * kPage * kVecBytes +
-                                                    static_cast<size_t>(within) * 32);
-      c0 = src[0];
-      c1 = src[1];
-    } else {
-      c0 = v4i{0, 0, 0, 0};
-      c1 = v4i{0, 0, 0, 0};
-    }
-    if (tid < 64) {
-      const int off = (tid & 15) * 16;
-      sc = scale_page >= 0
-               ? *reinterpret_cast<const v4i*>(k_scale + static_cast<size_t>(scale_page) * kPage * kVecScales + off)
-               : v4i{0, 0, 0, 0};
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* s_codes, uint8_t* s_scales) const {
-    const int tid = threadIdx.x;
-    const int pi = tid >> 7, within = tid & 127;
-    const int p = pi * kPage + (within >> 1), half = within & 1;
-    const int sw = chunk_swizzle(p);
-    uint8_t* dst = s_codes + p * kVecBytes;
-    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half) ^ sw)) = c0;
-    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half + 1) ^ sw)) = c1;
-    if (tid < 64) *reinterpret_cast<v4i*>(s_scales + (tid >> 4) * (kPage * kVecScales) + (tid & 15) * 16) = sc;
-  }
-};
+// Physical page of a page-table entry, or -1 when it is out of range.
+__device__ __forceinline__ int64_t page_or_neg(int32_t e, int64_t P_phys) { return (e >= 0 && e < P_phys) ? e : -1; }
 
 struct ScanArgs {
   const uint8_t* q;
@@ -243,8 +181,8 @@ struct SampleLoader {
   }
 
   __device__ __forceinline__ void resolve(int64_t P_phys) {
-    code_page = TileLoader::valid_or_neg(code_entry, P_phys);
-    scale_page = TileLoader::valid_or_neg(scale_entry, P_phys);
+    code_page = page_or_neg(code_entry, P_phys);
+    scale_page = page_or_neg(scale_entry, P_phys);
   }
 
   __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale) {
@@ -305,12 +243,98 @@ __device__ __forceinline__ void stream_with(Loader& ld, const ScanArgs& a, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Score-block streaming by direct global -> LDS loads (gfx950 LDS DMA), used by
+// every kernel that scores whole blocks. Wave w copies positions 32w .. 32w+31
+// of a block, which all lie in page w/2 of it: two 16-byte-per-lane loads for
+// the codes and one 4-byte-per-lane load (lanes 0-31) for the scales. A lane's
+// LDS destination is fixed by its lane id, so the chunk swizzle is applied on
+// the source side: the lane that fills chunk slot s of position p reads chunk
+// s ^ chunk_swizzle(p). Blocks are double-buffered (the copy of block i+1 runs
+// while block i is scored); page-table entries are read one block ahead.
+// Pages whose entry is out of range are not copied: row_prep rejected every row
+// whose window touches them, so no active row uses those positions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void vm_wait_all() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct BlockDma {
+  int src0, src1, src_sc;   // per-lane byte offsets inside a page
+  int wave;                 // wave-uniform
+  int run;                  // LDS byte offset of the wave's 32 positions
+
+  __device__ __forceinline__ void init(int w, int lane) {
+    wave = w;
+    const int pin = 32 * (w & 1), pq = lane >> 2, slot = lane & 3;
+    const int pb = 64 * (w >> 1) + pin + pq;   // block position of run 0 of this lane
+    src0 = (pin + pq) * kVecBytes + 16 * (slot ^ chunk_swizzle(pb));
+    src1 = (pin + 16 + pq) * kVecBytes + 16 * (slot ^ chunk_swizzle(pb + 16));
+    src_sc = (pin + (lane & 31)) * kVecScales;
+    run = 32 * w;
+  }
+
+  // Lane l holds the page-table entry of page l % 4 of block t (-1 beyond the table).
+  __device__ __forceinline__ static int32_t entries(const ScanArgs& a, int t, int lane) {
+    const int64_t lp = static_cast<int64_t>(t) * kTilePages + (lane & 3);
+    return lp < a.P_log ? a.page_table[lp] : -1;
+  }
+
+  __device__ __forceinline__ void issue(const ScanArgs& a, int32_t ent, uint8_t* codes, uint8_t* scales,
+                                        int lane) const {
+    const int32_t e = __builtin_amdgcn_readlane(ent, wave >> 1);
+    if (e < 0 || e >= a.P_phys) return;
+    const uint8_t* page = a.k_pages + static_cast<size_t>(e) * (kPage * kVecBytes);
+    __builtin_amdgcn_global_load_lds(page + src0, codes + run * kVecBytes, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(page + src1, codes + (run + 16) * kVecBytes, 16, 0, 0);
+    if (lane < 32)
+      __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e) * (kPage * kVecScales) + src_sc,
+                                       scales + run * kVecScales, 4, 0, 0);
+  }
+};
+
+// One step of the stream: start the copy of block i+1 into the other buffer,
+// score block i, then wait for the copy and for every wave.
 template <class Body>
-__device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t (*s_codes)[kTile * kVecBytes],
-                                              uint8_t (*s_scales)[kTile * kVecScales], Body&& body) {
-  TileLoader ld;
-  stream_with(ld, a, seq, s_codes, s_scales, static_cast<Body&&>(body));
+__device__ __forceinline__ void stream_step(const ScanArgs& a, const BlockSeq& seq, const BlockDma& d, int32_t& ent,
+                                            int i, int lane, const uint8_t* codes, const uint8_t* scales,
+                                            uint8_t* next_codes, uint8_t* next_scales, Body& body) {
+  if (i + 1 < seq.n) {
+    d.issue(a, ent, next_codes, next_scales, lane);
+    if (i + 2 < seq.n) ent = BlockDma::entries(a, seq.tile(i + 2), lane);
+  }
+  body(seq.tile(i), codes, scales);
+  vm_wait_all();
+  __syncthreads();
 }
+
+// The two buffers are separate LDS variables and the loop is unrolled by two,
+// so that every access names its buffer statically: the compiler then knows
+// that scoring one buffer does not read what the copy into the other writes,
+// and does not wait for that copy before the scoring's LDS reads.
+template <class Body>
+__device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t* codes0, uint8_t* scales0,
+                                              uint8_t* codes1, uint8_t* scales1, Body&& body) {
+  if (seq.n <= 0) return;
+  const int lane = threadIdx.x & 63;
+  BlockDma d;
+  d.init(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane);
+  int32_t ent = BlockDma::entries(a, seq.tile(0), lane);
+  vm_wait_all();
+  d.issue(a, ent, codes0, scales0, lane);
+  if (seq.n > 1) ent = BlockDma::entries(a, seq.tile(1), lane);
+  vm_wait_all();
+  __syncthreads();
+  for (int i = 0; i < seq.n; i += 2) {
+    stream_step(a, seq, d, ent, i, lane, codes0, scales0, codes1, scales1, body);
+    if (i + 1 < seq.n) stream_step(a, seq, d, ent, i + 1, lane, codes1, scales1, codes0, scales0, body);
+  }
+}
+
+// LDS of the block stream: two buffers of one score block each.
+#define MQA_BLOCK_BUFFERS                                                        \
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes0[kTile * kVecBytes];   \
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes1[kTile * kVecBytes];   \
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales0[kTile * kVecScales]; \
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales1[kTile * kVecScales]
 
 // Calls f(p0, blk) for each 64-position block of score block t that intersects
 // [start, end).
@@ -362,7 +386,7 @@ __global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandA
   __shared__ uint32_t s_hist[kRowsPerCta][256];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerCta + wave;
   const bool active = row < a.Q && a.row_state[row] == kRowLong;
   int start = 0, end = 0;
@@ -459,13 +483,14 @@ __global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandA
 // which the merge detects as an overflow.
 // ---------------------------------------------------------------------------
 template <int K>
-__global__ void __launch_bounds__(kCtaThreads, 2) scan_kernel(ScanArgs a, CandArgs c) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+// Four waves per SIMD (the second launch bound is a minimum of waves per SIMD):
+// two CTAs per CU, at most 128 VGPRs.
+__global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandArgs c) {
+  MQA_BLOCK_BUFFERS;
   __shared__ uint64_t s_stage[kRowsPerCta][kStageCap];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerCta + wave;
   bool active = row < a.Q && a.row_state[row] == kRowLong;
   int start = 0, end = 0;
@@ -504,12 +529,12 @@ __global__ void __launch_bounds__(kCtaThreads, 2) scan_kernel(ScanArgs a, CandAr
     sf = 0;
   };
   const LaneOffsets lo = lane_offsets(lane);
-  stream_blocks(a, seq, s_codes, s_scales, [&](int t, const uint8_t* codes, const uint8_t* scales) {
+  stream_blocks(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, [&](int t, const uint8_t* codes, const uint8_t* scales) {
     if (!active) return;
     const int tb = t * kTile;
     if (tb >= end || tb + kTile <= start) return;
     const bool inside = tb >= start && tb + kTile <= end;   // no window mask needed
-    score_block_pipelined(qr, codes, scales, lo, [&](int blk, float sc) {
+    score_block(qr, codes, scales, lo, [&](int blk, float sc) {
       const int pos = tb + 64 * blk + lane;
       const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
       bool pass = key > gate;
@@ -536,13 +561,12 @@ __global__ void __launch_bounds__(kCtaThreads, 2) scan_kernel(ScanArgs a, CandAr
 template <int K, int CAP, int FBS>
 __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs a, CandArgs c) {
   static_assert(CAP >= K + 64, "pool must hold K keys plus one batch");
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+  MQA_BLOCK_BUFFERS;
   __shared__ uint64_t s_pool[kRowsPerCta][CAP];
   __shared__ uint32_t s_hist[kRowsPerCta][256];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int listed = *c.fb_count;
   const int chunks = (listed + kRowsPerCta - 1) / kRowsPerCta;
   for (int item = blockIdx.x; item < chunks * FBS; item += gridDim.x) {
@@ -569,7 +593,7 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs 
     int fill = 0;
     uint64_t gate = 0;
     bool failed = false;
-    stream_blocks(a, seq, s_codes, s_scales, [&](int t, const uint8_t* codes, const uint8_t* scales) {
+    stream_blocks(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, [&](int t, const uint8_t* codes, const uint8_t* scales) {
       if (!active) return;
       for_blocks_in_window(t, start, end, [&](int p0, int blk) {
         const float sc = score64(qr, codes, scales, blk, lane);
@@ -928,12 +952,11 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
 // fused path, but every score inside an active row's window goes to
 // logits[row, s].
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kCtaThreads, 2) dense_score_kernel(ScanArgs a, float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+__global__ void __launch_bounds__(kCtaThreads, 4) dense_score_kernel(ScanArgs a, float* __restrict__ logits) {
+  MQA_BLOCK_BUFFERS;
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerCta + wave;
   const bool active = row < a.Q && a.row_state[row] == kRowLong;
   int start = 0, end = 0;
@@ -950,7 +973,7 @@ __global__ void __launch_bounds__(kCtaThreads, 2) dense_score_kernel(ScanArgs a,
               a.weights + static_cast<size_t>(row) * kHeads, lane);
   __builtin_amdgcn_s_waitcnt(0);
   float* out = logits + static_cast<size_t>(active ? row : 0) * (a.P_log * kPage);
-  stream_blocks(a, split_range(u0, u1, blockIdx.y, a.splits), s_codes, s_scales,
+  stream_blocks(a, split_range(u0, u1, blockIdx.y, a.splits), s_codes0, s_scales0, s_codes1, s_scales1,
                 [&](int t, const uint8_t* codes, const uint8_t* scales) {
                   if (!active) return;
                   for_blocks_in_window(t, start, end, [&](int p0, int blk) {
