@@ -248,7 +248,7 @@ def mqa_fp4_abi_version() -> int:
 
 
 def mqa_fp4_set_stage_events(events) -> None:
-    """Measurement hook: ``events`` is a ctypes array of 4 hipEvent_t handles
+    """Measurement hook: ``events`` is a ctypes array of 5 hipEvent_t handles
     (or None to turn the hook off); see the C header."""
     if events is None:
         _rc(lib().mqa_fp4_set_stage_events(None, 0), "mqa_fp4_set_stage_events")

@@ -253,9 +253,9 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   record_stage(1, st);
   for (int stage = 0; stage < 5 && rc == MQA_OK; ++stage) {
     rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_mode, stage, st));
-    if (stage == 1) record_stage(2, st);
+    if (stage <= 1) record_stage(2 + stage, st);   // after calibration, after the scan
   }
-  record_stage(3, st);
+  record_stage(4, st);
   return rc;
 }
 
@@ -315,10 +315,11 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   record_stage(1, st);
+  record_stage(2, st);   // no calibration on the dense path
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
-  record_stage(2, st);
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
   record_stage(3, st);
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
+  record_stage(4, st);
   return rc;
 }
 
@@ -417,7 +418,7 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n) {
     t_stage_events = nullptr;
     return MQA_OK;
   }
-  if (n != 4) return MQA_ERR_BAD_SIZE;
+  if (n != 5) return MQA_ERR_BAD_SIZE;
   t_stage_events = events;
   return MQA_OK;
 }

@@ -79,3 +79,13 @@ def test_dense_and_logits_entry_points_check_k_on_host(lib):
     p = P(0x1000)
     assert lib.mqa_fp4_dense_topk_prefill(p, p, 1, p, p, 1, p, p, 1, p, p, 7, p, p, p, p, None, None) == -1
     assert lib.mqa_fp4_logits_topk(p, 1, p, 1, 1, p, p, 100, p, p, p, None, None) == -1
+
+
+def test_stage_event_hook_takes_exactly_five_events(lib):
+    # The hook only stores the array (no HIP call): five handles are accepted,
+    # other counts are rejected, NULL / zero turns it off.
+    arr5 = (ctypes.c_void_p * 5)()
+    arr4 = (ctypes.c_void_p * 4)()
+    assert lib.mqa_fp4_set_stage_events(ctypes.cast(arr4, ctypes.c_void_p), 4) == -4
+    assert lib.mqa_fp4_set_stage_events(ctypes.cast(arr5, ctypes.c_void_p), 5) == 0
+    assert lib.mqa_fp4_set_stage_events(None, 0) == 0
