@@ -160,89 +160,6 @@ __device__ __forceinline__ BlockSeq split_range(int u0, int u1, int split, int s
   return BlockSeq{a, b - a};
 }
 
-// Gathers "sample blocks": block v holds the 256 positions base + 16 * (256 v + p),
-// p = 0..255 (base = first position of the row tile's range, a multiple of 256),
-// i.e. every 16th position, from 64 different pages. Same LDS image as a score
-// block, so score64() applies unchanged.
-struct SampleLoader {
-  v4i c0, c1;
-  int32_t sc;
-  int32_t code_entry, scale_entry;
-  int64_t code_page, scale_page;
-  int u0;
-
-  __device__ __forceinline__ void fetch_entries(const int32_t* pt, int64_t P_log, int v) {
-    const int tid = threadIdx.x;
-    const int64_t base_page = static_cast<int64_t>(u0) * kTilePages + static_cast<int64_t>(v) * 64;
-    const int64_t lp = base_page + ((tid >> 1) >> 2);
-    code_entry = lp < P_log ? pt[lp] : -1;
-    const int64_t slp = base_page + ((tid & 255) >> 2);
-    scale_entry = slp < P_log ? pt[slp] : -1;
-  }
-
-  __device__ __forceinline__ void resolve(int64_t P_phys) {
-    code_page = page_or_neg(code_entry, P_phys);
-    scale_page = page_or_neg(scale_entry, P_phys);
-  }
-
-  __device__ __forceinline__ void load(const uint8_t* k_pages, const uint8_t* k_scale) {
-    const int tid = threadIdx.x;
-    const int p = tid >> 1, half = tid & 1;
-    if (code_page >= 0) {
-      const v4i* src = reinterpret_cast<const v4i*>(k_pages + static_cast<size_t>(code_page) * kPage * kVecBytes +
-                                                    static_cast<size_t>(16 * (p & 3)) * kVecBytes + 32 * half);
-      c0 = src[0];
-      c1 = src[1];
-    } else {
-      c0 = v4i{0, 0, 0, 0};
-      c1 = v4i{0, 0, 0, 0};
-    }
-    if (tid < 256) {
-      const int ps = tid;
-      sc = scale_page >= 0 ? *reinterpret_cast<const int32_t*>(k_scale + static_cast<size_t>(scale_page) * kPage * kVecScales +
-                                                               static_cast<size_t>(16 * (ps & 3)) * kVecScales)
-                           : 0;
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t* s_codes, uint8_t* s_scales) const {
-    const int tid = threadIdx.x;
-    const int p = tid >> 1, half = tid & 1;
-    const int sw = chunk_swizzle(p);
-    uint8_t* dst = s_codes + p * kVecBytes;
-    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half) ^ sw)) = c0;
-    *reinterpret_cast<v4i*>(dst + 16 * ((2 * half + 1) ^ sw)) = c1;
-    if (tid < 256) *reinterpret_cast<int32_t*>(s_scales + tid * kVecScales) = sc;
-  }
-};
-
-// Streams the CTA's block sequence through LDS and calls
-// body(tile, s_codes, s_scales) for every block, for every wave (uniformly).
-template <class Loader, class Body>
-__device__ __forceinline__ void stream_with(Loader& ld, const ScanArgs& a, const BlockSeq& seq,
-                                            uint8_t (*s_codes)[kTile * kVecBytes],
-                                            uint8_t (*s_scales)[kTile * kVecScales], Body&& body) {
-  if (seq.n <= 0) return;
-  ld.fetch_entries(a.page_table, a.P_log, seq.tile(0));
-  ld.resolve(a.P_phys);
-  ld.load(a.k_pages, a.k_scale);
-  if (seq.n > 1) ld.fetch_entries(a.page_table, a.P_log, seq.tile(1));
-  ld.store(s_codes[0], s_scales[0]);
-  __syncthreads();
-  for (int i = 0; i < seq.n; ++i) {
-    const int buf = i & 1;
-    const bool more = i + 1 < seq.n;
-    if (more) {
-      ld.resolve(a.P_phys);
-      ld.load(a.k_pages, a.k_scale);
-      if (i + 2 < seq.n) ld.fetch_entries(a.page_table, a.P_log, seq.tile(i + 2));
-    }
-    body(seq.tile(i), s_codes[buf], s_scales[buf]);
-    if (more) ld.store(s_codes[buf ^ 1], s_scales[buf ^ 1]);
-    __syncthreads();
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Score-block streaming by direct global -> LDS loads (gfx950 LDS DMA), used by
 // every kernel that scores whole blocks. Wave w copies positions 32w .. 32w+31
@@ -260,7 +177,7 @@ __device__ __forceinline__ void vm_wait_all() { __asm__ __volatile__("s_waitcnt 
 struct BlockDma {
   int src0, src1, src_sc;   // per-lane byte offsets inside a page
   int wave;                 // wave-uniform
-  int run;                  // LDS byte offset of the wave's 32 positions
+  int run;                  // first block position of the wave's 32
 
   __device__ __forceinline__ void init(int w, int lane) {
     wave = w;
@@ -273,12 +190,14 @@ struct BlockDma {
   }
 
   // Lane l holds the page-table entry of page l % 4 of block t (-1 beyond the table).
-  __device__ __forceinline__ static int32_t entries(const ScanArgs& a, int t, int lane) {
-    const int64_t lp = static_cast<int64_t>(t) * kTilePages + (lane & 3);
+  // (Logical page indices fit in int32: the host checks 64 * P_log <= INT32_MAX.)
+  using Ent = int32_t;
+  __device__ __forceinline__ Ent entries(const ScanArgs& a, int t, int lane) const {
+    const int lp = t * kTilePages + (lane & 3);
     return lp < a.P_log ? a.page_table[lp] : -1;
   }
 
-  __device__ __forceinline__ void issue(const ScanArgs& a, int32_t ent, uint8_t* codes, uint8_t* scales,
+  __device__ __forceinline__ void issue(const ScanArgs& a, const Ent& ent, uint8_t* codes, uint8_t* scales,
                                         int lane) const {
     const int32_t e = __builtin_amdgcn_readlane(ent, wave >> 1);
     if (e < 0 || e >= a.P_phys) return;
@@ -291,42 +210,113 @@ struct BlockDma {
   }
 };
 
+// "Sample blocks" of the calibration: sample block v holds the positions
+// base + 16 * (256 v + p), p = 0..255 (base = first position of the row tile's
+// range, a multiple of 256), i.e. every 16th position, four per page. Same LDS
+// image as a score block (position p at slot p, same chunk swizzle), so the
+// block scorer applies unchanged. Every lane copies from its own page.
+struct SampleDma {
+  int base_pg;   // first logical page of the sampled range
+  int run;       // first block position of the wave's 32
+
+  __device__ __forceinline__ void init(int u0, int w, int) {
+    base_pg = u0 * kTilePages;
+    run = 32 * w;
+  }
+
+  // Per-lane source layout, recomputed at every use from a lane index the
+  // compiler cannot hoist (an opaque copy): the loop-invariant 64-bit per-lane
+  // addresses it would otherwise keep for the whole scan do not fit the
+  // 128-VGPR budget of four waves per SIMD.
+  struct Lane {
+    int pg0, pg1, pg_sc;      // page index inside a sample block (0..63)
+    int off0, off1, off_sc;   // byte offset inside the source page
+  };
+  __device__ __forceinline__ Lane lane_layout() const {
+    int lane;
+    __asm__ __volatile__("v_and_b32 %0, 63, %1" : "=v"(lane) : "v"(static_cast<int>(threadIdx.x)));
+    const int pq = lane >> 2, slot = lane & 3;
+    const int p0 = run + pq, p1 = p0 + 16, ps = run + (lane & 31);
+    return Lane{p0 >> 2, p1 >> 2, ps >> 2, kCalStride * (p0 & 3) * kVecBytes + 16 * (slot ^ chunk_swizzle(p0)),
+                kCalStride * (p1 & 3) * kVecBytes + 16 * (slot ^ chunk_swizzle(p1)),
+                kCalStride * (ps & 3) * kVecScales};
+  }
+
+  struct Ent {
+    int32_t e0, e1, es;
+  };
+  // Uniform base + 32-bit unsigned byte offset (lp < 2^25), so the load uses a
+  // scalar base and one offset VGPR per entry.
+  __device__ __forceinline__ static int32_t entry(const ScanArgs& a, int lp) {
+    const uint32_t off = static_cast<uint32_t>(lp) * 4u;
+    return lp < a.P_log ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(a.page_table) + off) : -1;
+  }
+  __device__ __forceinline__ Ent entries(const ScanArgs& a, int v, int) const {
+    const Lane l = lane_layout();
+    const int b = base_pg + v * (kTile / 4);   // sample block v spans 64 pages
+    return Ent{entry(a, b + l.pg0), entry(a, b + l.pg1), entry(a, b + l.pg_sc)};
+  }
+
+  __device__ __forceinline__ void issue(const ScanArgs& a, const Ent& e, uint8_t* codes, uint8_t* scales,
+                                        int lane) const {
+    const Lane l = lane_layout();
+    if (e.e0 >= 0 && e.e0 < a.P_phys)
+      __builtin_amdgcn_global_load_lds(a.k_pages + static_cast<size_t>(e.e0) * (kPage * kVecBytes) + l.off0,
+                                       codes + run * kVecBytes, 16, 0, 0);
+    if (e.e1 >= 0 && e.e1 < a.P_phys)
+      __builtin_amdgcn_global_load_lds(a.k_pages + static_cast<size_t>(e.e1) * (kPage * kVecBytes) + l.off1,
+                                       codes + (run + 16) * kVecBytes, 16, 0, 0);
+    if (lane < 32 && e.es >= 0 && e.es < a.P_phys)
+      __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e.es) * (kPage * kVecScales) + l.off_sc,
+                                       scales + run * kVecScales, 4, 0, 0);
+  }
+};
+
 // One step of the stream: start the copy of block i+1 into the other buffer,
 // score block i, then wait for the copy and for every wave.
-template <class Body>
-__device__ __forceinline__ void stream_step(const ScanArgs& a, const BlockSeq& seq, const BlockDma& d, int32_t& ent,
-                                            int i, int lane, const uint8_t* codes, const uint8_t* scales,
-                                            uint8_t* next_codes, uint8_t* next_scales, Body& body) {
+template <class Dma, class Body>
+__device__ __forceinline__ void stream_step(const ScanArgs& a, const BlockSeq& seq, const Dma& d,
+                                            typename Dma::Ent& ent, int i, int lane, const uint8_t* codes,
+                                            const uint8_t* scales, uint8_t* next_codes, uint8_t* next_scales,
+                                            Body& body) {
   if (i + 1 < seq.n) {
     d.issue(a, ent, next_codes, next_scales, lane);
-    if (i + 2 < seq.n) ent = BlockDma::entries(a, seq.tile(i + 2), lane);
+    if (i + 2 < seq.n) ent = d.entries(a, seq.tile(i + 2), lane);
   }
   body(seq.tile(i), codes, scales);
   vm_wait_all();
   __syncthreads();
 }
 
-// The two buffers are separate LDS variables and the loop is unrolled by two,
-// so that every access names its buffer statically: the compiler then knows
-// that scoring one buffer does not read what the copy into the other writes,
-// and does not wait for that copy before the scoring's LDS reads.
-template <class Body>
-__device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t* codes0, uint8_t* scales0,
-                                              uint8_t* codes1, uint8_t* scales1, Body&& body) {
+// Streams the blocks of seq through LDS and calls body(block, codes, scales)
+// for every block, in every wave (uniformly). The two buffers are separate LDS
+// variables and the loop is unrolled by two, so that every access names its
+// buffer statically: the compiler then knows that scoring one buffer does not
+// read what the copy into the other writes, and does not wait for that copy
+// before the scoring's LDS reads.
+template <class Dma, class Body>
+__device__ __forceinline__ void stream_dma(const ScanArgs& a, const Dma& d, const BlockSeq& seq, uint8_t* codes0,
+                                           uint8_t* scales0, uint8_t* codes1, uint8_t* scales1, Body&& body) {
   if (seq.n <= 0) return;
   const int lane = threadIdx.x & 63;
-  BlockDma d;
-  d.init(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane);
-  int32_t ent = BlockDma::entries(a, seq.tile(0), lane);
+  typename Dma::Ent ent = d.entries(a, seq.tile(0), lane);
   vm_wait_all();
   d.issue(a, ent, codes0, scales0, lane);
-  if (seq.n > 1) ent = BlockDma::entries(a, seq.tile(1), lane);
+  if (seq.n > 1) ent = d.entries(a, seq.tile(1), lane);
   vm_wait_all();
   __syncthreads();
   for (int i = 0; i < seq.n; i += 2) {
     stream_step(a, seq, d, ent, i, lane, codes0, scales0, codes1, scales1, body);
     if (i + 1 < seq.n) stream_step(a, seq, d, ent, i + 1, lane, codes1, scales1, codes0, scales0, body);
   }
+}
+
+template <class Body>
+__device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t* codes0, uint8_t* scales0,
+                                              uint8_t* codes1, uint8_t* scales1, Body&& body) {
+  BlockDma d;
+  d.init(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+  stream_dma(a, d, seq, codes0, scales0, codes1, scales1, static_cast<Body&&>(body));
 }
 
 // LDS of the block stream: two buffers of one score block each.
@@ -379,9 +369,8 @@ __device__ __forceinline__ int sample_keep(int K, int m, int n) {
 // both exist for testing.
 // ---------------------------------------------------------------------------
 template <int K>
-__global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandArgs c, int mode) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kTile * kVecBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t s_scales[2][kTile * kVecScales];
+__global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandArgs c, int mode) {
+  MQA_BLOCK_BUFFERS;
   __shared__ uint64_t s_pool[kRowsPerCta][kCalCap];
   __shared__ uint32_t s_hist[kRowsPerCta][256];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
@@ -416,21 +405,21 @@ __global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandA
   uint64_t gate = 0;
   bool bad = false;
   if (mode == 0) {
-    SampleLoader ld;
-    ld.u0 = u0;
+    SampleDma d;
+    d.init(u0, wave, lane);
+    const LaneOffsets lo = lane_offsets(lane);
     const BlockSeq seq{0, (u1 - u0 + kCalStride - 1) / kCalStride};
-    stream_with(ld, a, seq, s_codes, s_scales, [&](int v, const uint8_t* codes, const uint8_t* scales) {
+    stream_dma(a, d, seq, s_codes0, s_scales0, s_codes1, s_scales1,
+               [&](int v, const uint8_t* codes, const uint8_t* scales) {
       if (!gated) return;
-#pragma unroll 1
-      for (int blk = 0; blk < kTile / 64; ++blk) {
-        const int p0 = base + kCalStride * (kTile * v + 64 * blk);     // first position of these 64 samples
-        if (p0 >= end || p0 + kCalStride * 64 <= start) continue;
-        const float sc = score64(qr, codes, scales, blk, lane);
-        const int pos = p0 + kCalStride * lane;
+      const int vb = base + kCalStride * kTile * v;   // position of sample 0 of block v
+      if (vb >= end || vb + kCalStride * kTile <= start) return;
+      score_block(qr, codes, scales, lo, [&](int blk, float sc) {
+        const int pos = vb + kCalStride * (64 * blk + lane);
         const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
         bool pass = pos >= start && pos < end && key > gate;
         uint64_t msk = __ballot(pass);
-        if (msk == 0) continue;
+        if (msk == 0) return;
         int cnt = __popcll(msk);
         if (fill + cnt > kCalCap) {
           const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
@@ -443,7 +432,7 @@ __global__ void __launch_bounds__(kCtaThreads, 1) calib_kernel(ScanArgs a, CandA
         }
         if (pass) pool[fill + mbcnt64(msk)] = key;
         fill += cnt;
-      }
+      });
     });
   }
   if (!active) return;
