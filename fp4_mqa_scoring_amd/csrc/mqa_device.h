@@ -52,6 +52,26 @@ __device__ __forceinline__ float key_score(uint64_t k) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
+// Float prefilter for "key > gate": every key above the gate has upper 32 bits
+// >= those of the gate, and every score with such upper bits satisfies
+// !(score < gate_floor(gate)) (non-negative classes compare as floats, larger
+// bit patterns of negative scores are smaller magnitudes, -0 >= any negative
+// float, and a NaN gate class admits everything, NaN included). So the float
+// test is a superset of the exact key test and never drops a candidate.
+__device__ __forceinline__ float gate_floor(uint64_t gate) {
+  const uint32_t o = static_cast<uint32_t>(gate >> 32);
+  if (o == 0u) return -__builtin_inff();
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Lanes l of a 64-position run starting at p0 with start <= p0 + l < end.
+__device__ __forceinline__ uint64_t window_lanes(int p0, int start, int end) {
+  const int lo = min(max(start - p0, 0), 64), hi = min(max(end - p0, 0), 64);
+  const uint64_t below_hi = hi >= 64 ? ~0ull : ((1ull << hi) - 1ull);
+  const uint64_t below_lo = lo >= 64 ? ~0ull : ((1ull << lo) - 1ull);
+  return below_hi & ~below_lo;
+}
+
 // ---------------------------------------------------------------------------
 // Wave helpers (wave64).
 // ---------------------------------------------------------------------------

@@ -502,6 +502,7 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
               a.weights + static_cast<size_t>(row) * kHeads, lane);
   __builtin_amdgcn_s_waitcnt(0);
 
+  const float gate_f = gate_floor(gate);
   uint64_t* stage = s_stage[wave];
   uint64_t* dst = c.cand + static_cast<size_t>(active ? row : 0) * c.cap;
   int sf = 0;   // staged keys (wave-uniform)
@@ -524,15 +525,17 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
     if (tb >= end || tb + kTile <= start) return;
     const bool inside = tb >= start && tb + kTile <= end;   // no window mask needed
     score_block(qr, codes, scales, lo, [&](int blk, float sc) {
-      const int pos = tb + 64 * blk + lane;
-      const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
-      bool pass = key > gate;
-      if (!inside) pass = pass && pos >= start && pos < end;
-      const uint64_t msk = __ballot(pass);
+      const int p0 = tb + 64 * blk;
+      // wave-uniform window mask; one float compare rejects almost every lane
+      const uint64_t win = inside ? ~0ull : window_lanes(p0, start, end);
+      uint64_t msk = __ballot(!(sc < gate_f)) & win;
+      if (msk == 0) return;
+      const uint64_t key = make_key(sc, static_cast<uint32_t>(p0 + lane));
+      msk &= __ballot(key > gate);
       if (msk == 0) return;
       const int cnt = __popcll(msk);
       if (sf + cnt > kStageCap) flush();
-      if (pass) stage[sf + mbcnt64(msk)] = key;
+      if ((msk >> lane) & 1ull) stage[sf + mbcnt64(msk)] = key;
       sf += cnt;
     });
   });
