@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FLOP_PER_PAIR = 2 * 64 * 128          # MXFP4 MFMA work per scored (row, position) pair
+FLOP_PER_MFMA = 2 * 32 * 32 * 64      # one v_mfma_scale_f32_32x32x64_f8f6f4
 VALU_PER_PAIR = 2 * 64                # integer ReLU + fp32 FMA per head
 MXFP4_PEAK = 10.1e15                  # MI355X dense MXFP4 MFMA, FLOP/s
 VALU_PEAK = 157.3e12 / 2              # fp32 vector: 157.3 TFLOP/s = 78.65e12 FMA lane-ops/s
@@ -95,8 +96,16 @@ def cpu_baseline(inp, budget_s: float, seed: int):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": pairs / dt, "unit": "scored pairs/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "extrapolated_full_call_s": inp.scored_pairs() / (pairs / dt),
+            "extrapolation": "scored pairs of the whole call / the sample's pairs/s (not run)",
             "sample": f"{len(done)} full rows of the same workload ({pairs} scored pairs, "
                       f"{dt:.1f} s wall), float64 scores + full sort, OpenMP over positions"}
 
@@ -184,6 +193,23 @@ def main():
     kern_flops = pairs * FLOP_PER_PAIR / (kern * 1e-3)
     kern_valu = pairs * VALU_PER_PAIR / (kern * 1e-3)
 
+    # sustained peaks of this device under the same conditions (outside the timed region)
+    peaks = {}
+    p_blocks, p_iters = 2048, 2000
+    pout = torch.empty(p_blocks * 512, dtype=torch.float32, device=dev)
+    for kind, name, work in ((0, "mxfp4_mfma_tflops", p_blocks * 8 * p_iters * 4 * FLOP_PER_MFMA),
+                             (1, "fp32_fma_tops", p_blocks * 512 * p_iters * 64)):
+        for _ in range(2):
+            mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        peaks[name] = work / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12
+    del pout
+
     # alternating dense / fused pairs, outside the timed region
     dense = None
     if args.pairs > 0:
@@ -242,7 +268,13 @@ def main():
                      "unit": "TFLOP/s", "frac": kern_flops / MXFP4_PEAK, "traffic": traffic,
                      "kernel": f"scan_kernel<{K}>", "kernel_ms": kern,
                      "valu_frac": kern_valu / VALU_PEAK,
-                     "mfma_plus_valu_frac": pairs * SERIAL_PAIR_S / (kern * 1e-3)},
+                     "mfma_plus_valu_frac": pairs * SERIAL_PAIR_S / (kern * 1e-3),
+                     "measured_peak_tflops": peaks["mxfp4_mfma_tflops"],
+                     "frac_of_measured_peak": kern_flops / 1e12 / peaks["mxfp4_mfma_tflops"],
+                     "measured_fp32_fma_tops": peaks["fp32_fma_tops"],
+                     "mfma_plus_valu_frac_measured": pairs * (FLOP_PER_PAIR / (peaks["mxfp4_mfma_tflops"] * 1e12)
+                                                              + VALU_PER_PAIR / (peaks["fp32_fma_tops"] * 1e12))
+                                                     / (kern * 1e-3)},
         "mxfp4_tflops_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / 1e12,
         "mxfp4_peak_frac_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / MXFP4_PEAK,
         "stage_ms": {"row_prep": float(np.mean(prep_ms)), "calibration": float(np.mean(calib_ms)),

@@ -181,6 +181,16 @@ int32_t mqa_fp4_status(void* stream, int32_t* status);
  * synchronisation. Returns MQA_ERR_BAD_SIZE for other n. */
 int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
 
+/* Measurement hook: sustained-peak probes on `stream` (no operator work).
+ * kind 0: a pure MXFP4 MFMA loop, blocks x 8 waves x iters x 4
+ *         v_mfma_scale_f32_32x32x64_f8f6f4 (2*32*32*64 FLOP each);
+ * kind 1: a pure fp32 FMA loop, blocks x 512 lanes x iters x 64 FMAs.
+ * out: device float[blocks * 512], written once per lane (keeps the work live).
+ * MI355X's published peaks are quoted at 2.4 GHz; timing these launches gives
+ * the rates under the clocks the operator actually sees. Returns
+ * MQA_ERR_BAD_SIZE for another kind or non-positive blocks / iters. */
+int32_t mqa_fp4_peak_probe(int32_t kind, float* out, int32_t blocks, int32_t iters, void* stream);
+
 /* Static description of a return code. */
 const char* mqa_fp4_error_string(int32_t code);
 

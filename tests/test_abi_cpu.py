@@ -89,3 +89,12 @@ def test_stage_event_hook_takes_exactly_five_events(lib):
     assert lib.mqa_fp4_set_stage_events(ctypes.cast(arr4, ctypes.c_void_p), 4) == -4
     assert lib.mqa_fp4_set_stage_events(ctypes.cast(arr5, ctypes.c_void_p), 5) == 0
     assert lib.mqa_fp4_set_stage_events(None, 0) == 0
+
+
+def test_peak_probe_rejects_bad_arguments_on_host(lib):
+    p = ctypes.c_void_p(0x1000)
+    assert lib.mqa_fp4_peak_probe(2, p, 1, 1, None) == -4        # unknown kind
+    assert lib.mqa_fp4_peak_probe(0, p, 0, 1, None) == -4        # no blocks
+    assert lib.mqa_fp4_peak_probe(1, p, 1, 0, None) == -4        # no iterations
+    assert lib.mqa_fp4_peak_probe(0, None, 1, 1, None) == -2
+    assert lib.mqa_fp4_peak_probe(0, ctypes.c_void_p(0x1002), 1, 1, None) == -3

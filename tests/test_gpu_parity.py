@@ -181,6 +181,47 @@ def test_long_windows_use_the_gate_and_match_the_oracle():
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
 
 
+def test_scratch_is_independent_of_context_length():
+    """The device scratch of one fused call -- the high-water mark of the
+    device's default memory pool, where the library's stream-ordered scratch
+    lives (torch's own allocator does not use that pool) -- is the same at
+    C4 = 65,536 and 262,144 for the same Q and K, and covers the library's
+    own report of it."""
+    _need_gpu()
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    pool = ctypes.c_void_p()
+    assert hip.hipDeviceGetDefaultMemPool(ctypes.byref(pool), 0) == 0
+    used_high = 8                                   # hipMemPoolAttrUsedMemHigh
+    Q, K = 64, 1024
+    highs = []
+    for S in (65536, 262144):
+        inp = synth.make_inputs(Q, S, K, 777)
+        dev = gu.to_device(inp)
+        torch.cuda.synchronize()
+        zero = ctypes.c_uint64(0)
+        assert hip.hipMemPoolSetAttribute(pool, used_high, ctypes.byref(zero)) == 0
+        gu.run_fused(dev, K, with_score=False)
+        v = ctypes.c_uint64(0)
+        assert hip.hipMemPoolGetAttribute(pool, used_high, ctypes.byref(v)) == 0
+        highs.append(v.value)
+    assert highs[0] == highs[1] > 0, highs
+    assert highs[0] >= mqa.mqa_fp4_topk_scratch_bytes(Q, K), highs
+
+
+def test_peak_probes_run():
+    """The measurement probes launch and write every lane (no operator work)."""
+    _need_gpu()
+    import torch
+    out = torch.full((4 * 512,), float("nan"), dtype=torch.float32, device="cuda:0")
+    for kind in (0, 1):
+        out.fill_(float("nan"))
+        mqa.mqa_fp4_peak_probe(kind, out, 4, 8)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+
+
 def test_non_default_stream_gives_same_outputs():
     _need_gpu()
     import torch
