@@ -65,6 +65,12 @@ def lib():
                                       ctypes.c_int]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
+        L.oracle_e2m1_encode.restype = ctypes.c_int
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        L.oracle_mx_scale_byte.restype = ctypes.c_int
+        L.oracle_mx_scale_byte.argtypes = [P]
+        L.oracle_mx_quantize.restype = None
+        L.oracle_mx_quantize.argtypes = [P, i64, P, P]
         _lib = L
     return _lib
 
@@ -154,3 +160,38 @@ def topk_rows(inp, rows, K: int | None = None, nthreads: int = 0):
     for i, r in enumerate(rows):
         cnt[i], raw[i], sl[i], sc[i] = topk_row(inp, r, K, nthreads)
     return cnt, raw, sl, sc
+
+
+# --- MXFP4 quantisation (OCP MX conversion; see oracle.c) ------------------------
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().oracle_e2m1_encode(float(v)))
+
+
+def mx_quantize(x):
+    """float32 [..., 128*k or 32*k] -> (codes uint8 [..., 16*k], scales uint8 [..., k]) per
+    32-element block: OCP MX conversion with E2M1 elements and UE8M0 scales."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] % 32 == 0
+    nb = x.size // 32
+    codes = np.empty(nb * 16, np.uint8)
+    scales = np.empty(nb, np.uint8)
+    if nb:
+        lib().oracle_mx_quantize(_p(x), nb, _p(codes), _p(scales))
+    lead = x.shape[:-1]
+    k = x.shape[-1] // 32
+    return codes.reshape(*lead, 16 * k), scales.reshape(*lead, k)
+
+
+def mx_dequantize(codes, scales):
+    """Inverse view for tests: E2M1 codes and UE8M0 scales -> float64 values."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    lo = (codes & 15).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    el = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    table = np.array([e2m1_value(c) for c in range(16)])
+    vals = table[el]
+    sc = np.array([ue8m0_value(e) for e in range(256)])[scales.astype(np.int64)]
+    k = scales.shape[-1]
+    return (vals.reshape(*vals.shape[:-1], k, 32) * sc[..., None]).reshape(vals.shape)

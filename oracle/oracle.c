@@ -261,3 +261,72 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/* ---- MXFP4 quantisation: the producer of the path's FP4 inputs ------------
+ *
+ * The pages name the payload only ("FP4 E2M1 payload with UE8M0 scales", [P2]
+ * Scope); the rule that turns real values into it is the OCP Microscaling
+ * Formats (MX) v1.0 conversion of a vector of scalars into one MX block, read
+ * for E2M1 elements (largest element exponent emax = 2, largest magnitude 6)
+ * and a UE8M0 shared scale:
+ *   1. the shared exponent is floor(log2(max_i |V_i|)) - emax;
+ *   2. the scale is X = 2^(shared exponent);
+ *   3. every element is V_i / X rounded to the nearest E2M1 value, a tie going
+ *      to the code whose mantissa bit is 0, magnitudes beyond 6 saturating to 6,
+ *      and the sign kept (a negative value that rounds to zero is -0, code 8).
+ * Readings where that rule leaves the encoding open (listed in the design doc):
+ *   - the scale byte is shared + 127, clamped to [0, 254];
+ *   - a block whose elements are all zero gets scale byte 0 and the zero codes
+ *     of their signs;
+ *   - a block holding a NaN or an infinity gets scale byte 0xFF (the UE8M0 NaN)
+ *     and all-zero codes;
+ *   - element 2j of a block is the low nibble of byte j (as everywhere here).
+ * The division by X is exact (a power of two; a result below the float64
+ * normal range would be far below the first rounding boundary, 0.25).
+ */
+
+/* E2M1 code (0..15) of a real value already divided by the block scale. */
+int oracle_e2m1_encode(double v) {
+    const int neg = signbit(v) ? 1 : 0;
+    const double a = fabs(v);
+    int best = 0;
+    for (int m = 1; m < 8; ++m) {
+        const double dm = fabs(a - E2M1_VALUE[m]), db = fabs(a - E2M1_VALUE[best]);
+        if (dm < db || (dm == db && (m & 1) == 0)) best = m;
+    }
+    return best | (neg << 3);
+}
+
+/* Scale byte of one 32-element block (see the readings above). */
+int oracle_mx_scale_byte(const float* x) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+        if (!isfinite(x[i])) return 0xFF;
+        if (fabs((double)x[i]) > amax) amax = fabs((double)x[i]);
+    }
+    if (amax == 0.0) return 0;
+    int e2;
+    (void)frexp(amax, &e2);            /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+    int byte = (e2 - 1) - 2 + 127;
+    if (byte < 0) byte = 0;
+    if (byte > 254) byte = 254;
+    return byte;
+}
+
+/* n_blocks blocks of 32 floats -> 16 code bytes and one scale byte each. */
+void oracle_mx_quantize(const float* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales) {
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        const float* xb = x + 32 * b;
+        const int sb = oracle_mx_scale_byte(xb);
+        scales[b] = (uint8_t)sb;
+        for (int j = 0; j < 16; ++j) {
+            int lo = 0, hi = 0;
+            if (sb != 0xFF) {
+                const double X = ldexp(1.0, sb - 127);
+                lo = oracle_e2m1_encode((double)xb[2 * j] / X);
+                hi = oracle_e2m1_encode((double)xb[2 * j + 1] / X);
+            }
+            codes[16 * b + j] = (uint8_t)(lo | (hi << 4));
+        }
+    }
+}

@@ -32,6 +32,14 @@ MUTANTS = {
     "window_end_off_by_one": ("end > ORACLE_PAGE * P_log) return -1;", "end >= ORACLE_PAGE * P_log) return -1;"),
     "last_page_unchecked": ("p <= (end - 1) / ORACLE_PAGE; ++p)\n            if", "p < (end - 1) / ORACLE_PAGE; ++p)\n            if"),
     "selection_not_sorted": ("    qsort(out_raw, (size_t)K, sizeof(int32_t), cmp_i32);\n", ""),
+    # MXFP4 quantiser
+    "quant_ties_away_from_zero": ("if (dm < db || (dm == db && (m & 1) == 0)) best = m;", "if (dm <= db) best = m;"),
+    "quant_emax_3": ("int byte = (e2 - 1) - 2 + 127;", "int byte = (e2 - 1) - 3 + 127;"),
+    "quant_exponent_rounded_up": ("int byte = (e2 - 1) - 2 + 127;", "int byte = e2 - 2 + 127;"),
+    "quant_negative_zero_lost": ("const int neg = signbit(v) ? 1 : 0;", "const int neg = v < 0.0 ? 1 : 0;"),
+    "quant_nibbles_swapped": ("codes[16 * b + j] = (uint8_t)(lo | (hi << 4));", "codes[16 * b + j] = (uint8_t)(hi | (lo << 4));"),
+    "quant_infinity_not_flagged": ("if (!isfinite(x[i])) return 0xFF;", "if (isnan(x[i])) return 0xFF;"),
+    "quant_scale_not_clamped": ("if (byte < 0) byte = 0;", ""),
 }
 
 
@@ -47,6 +55,7 @@ def test_mutant_is_caught(name, tmp_path):
                     "-lm"], check=True)
     env = dict(os.environ, MQA_ORACLE_LIB=str(so))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_quant_oracle.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
