@@ -110,6 +110,104 @@ def cpu_baseline(inp, budget_s: float, seed: int):
                       f"{dt:.1f} s wall), float64 scores + full sort, OpenMP over positions"}
 
 
+QUANT_BYTES = 128 * 4 + 64 + 4          # fp32 vector in, codes + scales out
+CACHE_WRITE_BYTES = QUANT_BYTES + 4 + 4 # + logical position + page-table entry
+
+
+def bench_quantize(args, torch, mqa, dev):
+    """The producer of the operator's inputs at the headline shape: quantise the
+    query tensor [8192, 64, 128] and write the C4 key cache of 196,608 positions
+    through a shuffled page table. HBM-bound; one step = both launches."""
+    Q, S = 8192, 196608
+    g = torch.Generator(device=dev).manual_seed(20261202)
+    xq = torch.randn((Q * 64, 128), generator=g, device=dev, dtype=torch.float32)
+    xk = torch.randn((S, 128), generator=g, device=dev, dtype=torch.float32)
+    P = S // 64
+    page_table = torch.randperm(P, generator=g, device=dev).to(torch.int32)
+    positions = torch.arange(S, dtype=torch.int32, device=dev)
+    qc = torch.empty((Q * 64, 64), dtype=torch.uint8, device=dev)
+    qs = torch.empty((Q * 64, 4), dtype=torch.uint8, device=dev)
+    kp = torch.empty((P, 64, 64), dtype=torch.uint8, device=dev)
+    ks = torch.empty((P, 64, 4), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        mqa.mqa_fp4_quantize(xq, qc, qs, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        mqa.mqa_fp4_cache_write(xk, positions, page_table, kp, ks, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    w_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    assert mqa.mqa_fp4_status(stream) == 0
+    # practical ceiling for context: a plain device copy of the quantiser's input bytes
+    y = torch.empty_like(xq)
+    for _ in range(3):
+        y.copy_(xq)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        y.copy_(xq)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * xq.numel() * 4 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    del y
+    q_bytes = Q * 64 * QUANT_BYTES
+    w_bytes = S * CACHE_WRITE_BYTES
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "mx_quantize_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as fh:
+            tr = json.load(fh)
+        src = os.path.join(ROOT, "fp4_mqa_scoring_amd", "csrc", "mqa_quant.hip")
+        with open(src, "rb") as fh:
+            if tr.get("kernel_source_hash") == hashlib.sha256(fh.read()).hexdigest()[:16]:
+                traffic = tr.get("bytes_per_launch")
+    line = {
+        "metric": "GB/s, MXFP4 quantisation of the query tensor + C4 cache write (headline shape)",
+        "value": (q_bytes + w_bytes) / (wall_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 -> mxfp4 (e2m1 + ue8m0)", "data": "synthetic",
+        "config": {"workload": f"quantise q [{Q}, 64, 128] + write C4 cache of {S} positions",
+                   "vectors_quantised": Q * 64, "cache_positions": S},
+        "roofline": {"bound": "hbm", "achieved": q_bytes / (q_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": q_bytes / (q_ms * 1e-3) / HBM_PEAK, "traffic": traffic,
+                     "kernel": "mx_quantize_kernel (quantise)", "kernel_ms": q_ms,
+                     "cache_write_ms": w_ms,
+                     "cache_write_gbs": w_bytes / (w_ms * 1e-3) / 1e9,
+                     "cache_write_frac": w_bytes / (w_ms * 1e-3) / HBM_PEAK,
+                     "device_copy_gbs": copy_gbs},
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        import oracle
+        xs = xq[: 1 << 16].cpu().numpy()
+        t1, nvec = time.perf_counter(), 0
+        while time.perf_counter() - t1 < min(args.cpu_budget, 10.0):
+            oracle.mx_quantize(xs)
+            nvec += xs.shape[0]
+        dt = time.perf_counter() - t1
+        line["cpu_baseline"] = {"value": nvec * QUANT_BYTES / dt / 1e9, "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{nvec} vectors (65,536 per pass of the same query tensor), "
+                                          f"{dt:.1f} s wall, single-threaded C"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +219,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     ap.add_argument("--splits", type=int, default=0, help="override context splits (0 = automatic)")
+    ap.add_argument("--op", default="topk", choices=("topk", "quantize"),
+                    help="topk: the fused operator (default); quantize: the MXFP4 quantiser and the C4 cache "
+                         "writer on the headline call's query tensor and cache")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -138,6 +239,18 @@ def main():
     mqa.lib()                          # fail loudly if the HIP library is not built
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    # one plain device copy of known size first, to scale the byte counters
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    if args.op == "quantize":
+        bench_quantize(args, torch, mqa, dev)
+        return
     cfg = args.workload if args.workload == "H" else int(args.workload)
     inp = synth.make_config(cfg)
     Q, S, K = inp.Q, inp.S, inp.K
@@ -147,14 +260,6 @@ def main():
     out_raw, out_slot, out_count = mqa.alloc_outputs(Q, K, dev)
     stream = torch.cuda.current_stream(dev)
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
 
     def fused():
         mqa.mqa_fp4_topk_prefill_ex(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"],

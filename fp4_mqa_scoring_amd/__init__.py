@@ -66,10 +66,12 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_abi_version.argtypes = []
         L.mqa_fp4_set_stage_events.argtypes = [P, i32]
         L.mqa_fp4_peak_probe.argtypes = [i32, P, i32, i32, P]
+        L.mqa_fp4_quantize.argtypes = [P, i64, P, P, P]
+        L.mqa_fp4_cache_write.argtypes = [P, i64, P, P, i64, i64, P, P, P]
         for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
                      "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events",
-                     "mqa_fp4_peak_probe"):
+                     "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -247,6 +249,45 @@ def mqa_fp4_status(stream=None, device=None) -> int:
 
 def mqa_fp4_abi_version() -> int:
     return int(lib().mqa_fp4_abi_version())
+
+
+def mqa_fp4_quantize(x, codes=None, scales=None, stream=None):
+    """MXFP4 quantisation (OCP MX conversion, E2M1 + UE8M0) of float32 x [..., 128]
+    into codes uint8 [..., 64] and scales uint8 [..., 4] (allocated if None)."""
+    import torch
+    _check(x, "x", torch.float32)
+    if x.shape[-1] != 128:
+        raise ValueError("x must end in 128 elements")
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (64,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (4,), dtype=torch.uint8, device=x.device)
+    _check(codes, "codes", torch.uint8)
+    _check(scales, "scales", torch.uint8)
+    n = x.numel() // 128
+    if codes.numel() != n * 64 or scales.numel() != n * 4:
+        raise ValueError("codes / scales do not match x")
+    _rc(lib().mqa_fp4_quantize(_ptr(x), n, _ptr(codes), _ptr(scales), _stream(stream, x.device)),
+        "mqa_fp4_quantize")
+    return codes, scales
+
+
+def mqa_fp4_cache_write(k, positions, page_table, k_pages, k_scale, stream=None) -> None:
+    """Quantise float32 keys k [n, 128] into the paged C4 cache at logical
+    positions (int32 [n]) through page_table (int32 [P_log])."""
+    import torch
+    _check(k, "k", torch.float32)
+    _check(positions, "positions", torch.int32)
+    _check(page_table, "page_table", torch.int32)
+    _check(k_pages, "k_pages", torch.uint8)
+    _check(k_scale, "k_scale", torch.uint8)
+    n = k.numel() // 128
+    if positions.numel() != n:
+        raise ValueError("positions must have one entry per key vector")
+    _rc(lib().mqa_fp4_cache_write(_ptr(k), n, _ptr(positions), _ptr(page_table), page_table.numel(),
+                                  k_pages.shape[0], _ptr(k_pages), _ptr(k_scale), _stream(stream, k.device)),
+        "mqa_fp4_cache_write")
 
 
 def mqa_fp4_peak_probe(kind: int, out, blocks: int, iters: int, stream=None) -> None:

@@ -423,6 +423,39 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n) {
   return MQA_OK;
 }
 
+int32_t mqa_fp4_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (n_vec < 0 || n_vec > (static_cast<int64_t>(1) << 40)) return MQA_ERR_BAD_SIZE;
+  const bool any = n_vec > 0;
+  const PtrSpec specs[] = {{x, any, 16}, {codes, any, 2}, {scales, any, 1}};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard guard;
+  DeviceInfo info;
+  const int32_t rc = enter(st, specs, 3, guard, &info);
+  if (rc != MQA_OK || !any) return rc;
+  return hip_rc(mqa::launch_mx_quantize(x, n_vec, codes, scales, nullptr, nullptr, 0, 0, info.cus, st));
+}
+
+int32_t mqa_fp4_cache_write(const float* k, int64_t n, const int32_t* positions, const int32_t* page_table,
+                            int64_t num_logical_pages, int64_t num_phys_pages, uint8_t* k_pages, uint8_t* k_scale,
+                            void* stream) {
+  if (n < 0 || n > 0x7FFFFFFFll) return MQA_ERR_BAD_SIZE;
+  int32_t rc = check_sizes(0, num_phys_pages, num_logical_pages);
+  if (rc != MQA_OK) return rc;
+  const bool any = n > 0;
+  const PtrSpec specs[] = {{k, any, 16},
+                           {positions, any, 4},
+                           {page_table, any && num_logical_pages > 0, 4},
+                           {k_pages, any && num_phys_pages > 0, 16},
+                           {k_scale, any && num_phys_pages > 0, 16}};
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, 5, guard, &info);
+  if (rc != MQA_OK || !any) return rc;
+  return hip_rc(mqa::launch_mx_quantize(k, n, k_pages, k_scale, positions, page_table, num_logical_pages,
+                                        num_phys_pages, info.cus, st));
+}
+
 const char* mqa_fp4_error_string(int32_t code) {
   switch (code) {
     case MQA_OK: return "ok";

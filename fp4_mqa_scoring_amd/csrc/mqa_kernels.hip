@@ -1143,6 +1143,15 @@ hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int3
   return hipGetLastError();
 }
 
+int32_t* status_word() {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_status)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return static_cast<int32_t*>(p);
+}
+
 hipError_t status_take(hipStream_t st, int32_t* host_out) {
   int32_t zero = 0;
   hipError_t e = hipMemcpyFromSymbolAsync(host_out, HIP_SYMBOL(g_status), sizeof(int32_t), 0,

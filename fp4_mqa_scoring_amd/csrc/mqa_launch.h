@@ -54,5 +54,14 @@ hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int3
                               hipStream_t st);
 // Copies the sticky status word to *host_out and clears it (synchronises st).
 hipError_t status_take(hipStream_t st, int32_t* host_out);
+// Device address of the current device's sticky status word (nullptr on error).
+int32_t* status_word();
+
+// MXFP4 quantisation of n_vec 128-element fp32 vectors (OCP MX conversion). With
+// positions == nullptr vector v goes to row v of codes / scales; otherwise to
+// the physical slot of logical C4 position positions[v] (cache writer).
+hipError_t launch_mx_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t* scales,
+                              const int32_t* positions, const int32_t* page_table, int64_t P_log, int64_t P_phys,
+                              int cus, hipStream_t st);
 
 }  // namespace mqa

@@ -181,6 +181,40 @@ int32_t mqa_fp4_status(void* stream, int32_t* status);
  * synchronisation. Returns MQA_ERR_BAD_SIZE for other n. */
 int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
 
+/*
+ * MXFP4 quantisation: the producer of the FP4 inputs above. Source: the
+ * payload named in "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK" (ROCm/aiter
+ * PR 5282), Scope (FP4 E2M1 with UE8M0 scales); the conversion rule is the OCP
+ * Microscaling Formats (MX) v1.0 conversion of a vector of scalars to an MX block,
+ * for E2M1 elements: per 32-element block, shared exponent floor(log2 max|v|) - 2,
+ * elements v / 2^shared rounded to the nearest E2M1 value with ties to the even
+ * mantissa bit, saturating at +-6, sign kept (-0 is code 8). Scale byte = shared
+ * + 127 clamped to [0, 254]; an all-zero block gets byte 0; a block holding a NaN
+ * or an infinity gets byte 0xFF (UE8M0 NaN) and zero codes.
+ *   x      float [n_vec, 128] (16-byte aligned)   e.g. q as [Q * 64, 128]
+ *   codes  uint8 [n_vec, 64]  (2-byte aligned)    element 2j = low nibble of byte j
+ *   scales uint8 [n_vec, 4]
+ * All device pointers on one gfx950 device, owned by the caller. HBM-bound: 512
+ * bytes read, 68 written per vector. Errors as for the operator (host-detected,
+ * nothing launched).
+ */
+int32_t mqa_fp4_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * C4 paged key-cache writer: quantises n fp32 key vectors k [n, 128] as above and
+ * stores vector i at logical C4 position positions[i], i.e. in row
+ * page_table[p / 64] * 64 + p % 64 of k_pages [P_phys, 64, 64] / k_scale
+ * [P_phys, 64, 4] (the operator's cache layout; "[FlyDSL][DSv4] Prototype FP4 MQA
+ * streaming TopK", Changes: raw C4 positions map through the page table). A
+ * vector whose position is outside [0, 64 * P_log) is not written and sets
+ * MQA_STATUS_BAD_WINDOW; one whose page maps outside [0, P_phys) is not written
+ * and sets MQA_STATUS_BAD_PAGE (read with mqa_fp4_status). Positions must be
+ * distinct within a call (which of two vectors lands at one slot is unspecified).
+ */
+int32_t mqa_fp4_cache_write(const float* k, int64_t n, const int32_t* positions, const int32_t* page_table,
+                            int64_t num_logical_pages, int64_t num_phys_pages, uint8_t* k_pages, uint8_t* k_scale,
+                            void* stream);
+
 /* Measurement hook: sustained-peak probes on `stream` (no operator work).
  * kind 0: a pure MXFP4 MFMA loop, blocks x 8 waves x iters x 4
  *         v_mfma_scale_f32_32x32x64_f8f6f4 (2*32*32*64 FLOP each);

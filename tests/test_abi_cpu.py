@@ -98,3 +98,17 @@ def test_peak_probe_rejects_bad_arguments_on_host(lib):
     assert lib.mqa_fp4_peak_probe(1, p, 1, 0, None) == -4        # no iterations
     assert lib.mqa_fp4_peak_probe(0, None, 1, 1, None) == -2
     assert lib.mqa_fp4_peak_probe(0, ctypes.c_void_p(0x1002), 1, 1, None) == -3
+
+
+def test_quantizer_and_cache_writer_reject_bad_arguments_on_host(lib):
+    P = ctypes.c_void_p
+    a = P(0x1000)
+    assert lib.mqa_fp4_quantize(a, -1, a, a, None) == -4
+    assert lib.mqa_fp4_quantize(None, 4, a, a, None) == -2
+    assert lib.mqa_fp4_quantize(a, 4, None, a, None) == -2
+    assert lib.mqa_fp4_quantize(P(0x1004), 4, a, a, None) == -3        # x needs 16-byte alignment
+    assert lib.mqa_fp4_quantize(a, 4, P(0x1001), a, None) == -3        # codes need 2-byte alignment
+    assert lib.mqa_fp4_cache_write(a, -1, a, a, 1, 1, a, a, None) == -4
+    assert lib.mqa_fp4_cache_write(a, 4, a, a, -1, 1, a, a, None) == -4
+    assert lib.mqa_fp4_cache_write(a, 4, None, a, 1, 1, a, a, None) == -2
+    assert lib.mqa_fp4_cache_write(a, 4, a, a, 1, 1, P(0x1008), a, None) == -3
