@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="H", help="H (headline) or 1..5")
     ap.add_argument("--pairs", type=int, default=15, help="alternating dense/fused pairs (0 = skip dense)")
+    ap.add_argument("--tiled-pairs", type=int, default=5,
+                    help="alternating context-tiled/fused pairs (0 = skip the tiled comparator)")
+    ap.add_argument("--tile", type=int, default=0, help="positions per tile of the tiled comparator (0 = 4096)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
@@ -346,6 +349,37 @@ def main():
                  "dense_logits_bytes": Q * S * 4}
         del logits
 
+    # alternating context-tiled / fused pairs, outside the timed region
+    tiled = None
+    if args.tiled_pairs > 0:
+        t_out = mqa.alloc_outputs(Q, K, dev)
+
+        def tiled_call():
+            mqa.mqa_fp4_tiled_topk_prefill(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"],
+                                           t["page_table"], t["row_start"], t["row_end"], K, *t_out,
+                                           tile_positions=args.tile, stream=stream)
+        tms, fms = [], []
+        for i in range(2 + args.tiled_pairs):
+            torch.cuda.synchronize()
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s2 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            tiled_call()
+            s1.record(stream)
+            fused()
+            s2.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                tms.append(s0.elapsed_time(s1))
+                fms.append(s1.elapsed_time(s2))
+        same = bool(torch.equal(t_out[0], out_raw) and torch.equal(t_out[2], out_count))
+        tiled = {"tiled_ms_median": float(np.median(tms)), "fused_ms_median": float(np.median(fms)),
+                 "pairs": args.tiled_pairs, "tile_positions": args.tile or 4096,
+                 "tiled_scratch_bytes": mqa.mqa_fp4_tiled_scratch_bytes(Q, K, args.tile),
+                 "tiled_equals_fused": same}
+        del t_out
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as fh:
@@ -387,6 +421,7 @@ def main():
                      "call_events": float(np.mean(call_ms))},
         "scratch_bytes": mqa.mqa_fp4_topk_scratch_bytes(Q, K, 0),
         "dense_comparator": dense,
+        "tiled_comparator": tiled,
         "checks_ok": ok,
     }
     key = (Q, S, K)

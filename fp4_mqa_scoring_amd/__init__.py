@@ -67,11 +67,15 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_set_stage_events.argtypes = [P, i32]
         L.mqa_fp4_peak_probe.argtypes = [i32, P, i32, i32, P]
         L.mqa_fp4_quantize.argtypes = [P, i64, P, P, P]
+        L.mqa_fp4_tiled_topk_prefill.argtypes = prefill[:11] + [i32, i32, P, P, P, P, P]
+        L.mqa_fp4_tiled_scratch_bytes.argtypes = [i64, i32, i32]
+        L.mqa_fp4_tiled_scratch_bytes.restype = i64
         L.mqa_fp4_cache_write.argtypes = [P, i64, P, P, i64, i64, P, P, P]
         for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
                      "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events",
-                     "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write"):
+                     "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write",
+                     "mqa_fp4_tiled_topk_prefill"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -190,6 +194,25 @@ def mqa_fp4_dense_topk_prefill(q, q_scale, k_pages, k_scale, weights, page_table
         _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), _ptr(logits), _ptr(out_raw),
         _ptr(out_slot), _ptr(out_count), _ptr(out_score), _stream(stream, q.device))
     _rc(rc, "mqa_fp4_dense_topk_prefill")
+
+
+def mqa_fp4_tiled_topk_prefill(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,
+                               out_raw, out_slot, out_count, out_score=None, tile_positions=0, stream=None):
+    """Bounded context-tiled exact TopK (same contract and outputs as the fused path)."""
+    Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    rc = lib().mqa_fp4_tiled_topk_prefill(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), P_phys, _ptr(weights),
+        _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), int(tile_positions), _ptr(out_raw),
+        _ptr(out_slot), _ptr(out_count), _ptr(out_score), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_tiled_topk_prefill")
+
+
+def mqa_fp4_tiled_scratch_bytes(num_rows: int, K: int, tile_positions: int = 0) -> int:
+    r = int(lib().mqa_fp4_tiled_scratch_bytes(int(num_rows), int(K), int(tile_positions)))
+    if r < 0:
+        raise MQAError(r, "mqa_fp4_tiled_scratch_bytes")
+    return r
 
 
 def mqa_fp4_dense_logits(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, logits,

@@ -144,6 +144,8 @@ int32_t auto_splits(int64_t Q, int cus, int per_cu = 2) {
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+constexpr int32_t kDefaultTile = 4096;   // positions per tile of the context-tiled path
+
 struct FusedScratch {
   size_t state_off, gate_off, count_off, list_off, listn_off, fbcnt_off, cand_off, total;
 };
@@ -421,6 +423,67 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n) {
   if (n != 5) return MQA_ERR_BAD_SIZE;
   t_stage_events = events;
   return MQA_OK;
+}
+
+int32_t mqa_fp4_tiled_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                   const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                                   const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                                   const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                   int32_t tile_positions, int32_t* out_raw, int32_t* out_slot,
+                                   int32_t* out_count, float* out_score, void* stream) {
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (tile_positions == 0) tile_positions = kDefaultTile;
+  if (tile_positions < 0 || tile_positions % 256 != 0 || tile_positions > (1 << 22)) return MQA_ERR_BAD_SIZE;
+  int32_t rc = check_sizes(num_rows, num_phys_pages, num_logical_pages);
+  if (rc != MQA_OK) return rc;
+  const bool rows = num_rows > 0;
+  const PtrSpec specs[] = {
+      {q, rows, 16},       {q_scale, rows, 4},   {k_pages, num_phys_pages > 0, 16},
+      {k_scale, num_phys_pages > 0, 16}, {weights, rows, 4}, {page_table, num_logical_pages > 0, 4},
+      {row_start, rows, 4}, {row_end, rows, 4},  {out_raw, rows, 4},
+      {out_slot, rows, 4}, {out_count, rows, 4}, {out_score, false, 4},
+  };
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  if (rc != MQA_OK || !rows) return rc;
+  const PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  page_table,
+                   num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  const size_t Qz = static_cast<size_t>(num_rows);
+  const size_t state_b = align_up(Qz * sizeof(int32_t));
+  const size_t count_b = align_up(Qz * sizeof(int32_t));
+  const size_t run_b = align_up(Qz * static_cast<size_t>(K) * sizeof(uint64_t));
+  const size_t tile_b = align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float));
+  Scratch scratch;
+  rc = scratch.alloc(state_b + count_b + run_b + tile_b, st);
+  if (rc != MQA_OK) return rc;
+  char* base = static_cast<char*>(scratch.p);
+  int32_t* row_state = reinterpret_cast<int32_t*>(base);
+  int32_t* run_count = reinterpret_cast<int32_t*>(base + state_b);
+  uint64_t* running = reinterpret_cast<uint64_t*>(base + state_b + count_b);
+  float* tile_logits = reinterpret_cast<float*>(base + state_b + count_b + run_b);
+  record_stage(0, st);
+  rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
+  record_stage(1, st);
+  record_stage(2, st);
+  if (rc == MQA_OK)
+    rc = hip_rc(mqa::launch_tiled(p, row_state, auto_splits(num_rows, info.cus), tile_positions, tile_logits,
+                                  running, run_count, st));
+  record_stage(3, st);
+  record_stage(4, st);
+  return rc;
+}
+
+int64_t mqa_fp4_tiled_scratch_bytes(int64_t num_rows, int32_t K, int32_t tile_positions) {
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (tile_positions == 0) tile_positions = kDefaultTile;
+  if (num_rows < 0 || tile_positions < 0 || tile_positions % 256 != 0 || tile_positions > (1 << 22))
+    return MQA_ERR_BAD_SIZE;
+  const size_t Qz = static_cast<size_t>(num_rows);
+  return static_cast<int64_t>(2 * align_up(Qz * sizeof(int32_t)) +
+                              align_up(Qz * static_cast<size_t>(K) * sizeof(uint64_t)) +
+                              align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float)));
 }
 
 int32_t mqa_fp4_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t* scales, void* stream) {

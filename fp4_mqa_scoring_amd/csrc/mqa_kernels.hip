@@ -944,17 +944,22 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
 // fused path, but every score inside an active row's window goes to
 // logits[row, s].
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(kCtaThreads, 4) dense_score_kernel(ScanArgs a, float* __restrict__ logits) {
+// Scores of the positions in [lo, hi) of every active row's window go to
+// logits[row * ld + (pos - lo)]: the dense comparator uses [0, S) with ld = S,
+// the context-tiled path one tile [lo, lo + ld) at a time.
+__global__ void __launch_bounds__(kCtaThreads, 4) dense_score_kernel(ScanArgs a, float* __restrict__ logits,
+                                                                     int64_t ld, int32_t lo, int32_t hi) {
   MQA_BLOCK_BUFFERS;
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerCta + wave;
-  const bool active = row < a.Q && a.row_state[row] == kRowLong;
+  bool active = row < a.Q && a.row_state[row] == kRowLong;
   int start = 0, end = 0;
   if (active) {
-    start = a.row_start[row];
-    end = a.row_end[row];
+    start = max(a.row_start[row], lo);
+    end = min(a.row_end[row], hi);
+    active = start < end;
   }
   int u0 = 0, u1 = 0;
   if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
@@ -964,14 +969,14 @@ __global__ void __launch_bounds__(kCtaThreads, 4) dense_score_kernel(ScanArgs a,
               a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
               a.weights + static_cast<size_t>(row) * kHeads, lane);
   __builtin_amdgcn_s_waitcnt(0);
-  float* out = logits + static_cast<size_t>(active ? row : 0) * (a.P_log * kPage);
+  float* out = logits + static_cast<size_t>(active ? row : 0) * ld;   // column pos - lo
   stream_blocks(a, split_range(u0, u1, blockIdx.y, a.splits), s_codes0, s_scales0, s_codes1, s_scales1,
                 [&](int t, const uint8_t* codes, const uint8_t* scales) {
                   if (!active) return;
                   for_blocks_in_window(t, start, end, [&](int p0, int blk) {
                     const float sc = score64(qr, codes, scales, blk, lane);
                     const int pos = p0 + lane;
-                    if (pos >= start && pos < end) __builtin_nontemporal_store(sc, out + pos);
+                    if (pos >= start && pos < end) __builtin_nontemporal_store(sc, out + (pos - lo));
                   });
                 });
 }
@@ -1022,6 +1027,99 @@ __global__ void __launch_bounds__(1024) logits_topk_kernel(
 }
 
 // Gated candidate buffer per row, and the fallback's pool and splits.
+// ---------------------------------------------------------------------------
+// Bounded context-tiled exact TopK ("[FlyDSL][DSv4] Prototype FP4 MQA streaming
+// TopK", Changes: a bounded context-tiled implementation as the correctness /
+// reference fallback). The context is visited in tiles of `tile` positions; the
+// dense scorer writes one tile's fp32 scores of every row into a [Q, tile]
+// buffer, then each row merges its running exact top-K (at most K keys, same
+// total order) with the tile's keys by an exact radix select. Every position of
+// a window is seen in exactly one tile, so after the last tile the running set
+// is the window's top-K. No gate, no calibration; scratch Q * (4 tile + 8 K)
+// bytes, independent of the context length.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) tile_reset_kernel(int32_t* __restrict__ run_count, int64_t Q) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < Q) run_count[i] = 0;
+}
+
+template <int K>
+__global__ void __launch_bounds__(256) tile_merge_kernel(const int32_t* __restrict__ row_state,
+                                                         const int32_t* __restrict__ row_start,
+                                                         const int32_t* __restrict__ row_end,
+                                                         const float* __restrict__ tile_logits, int32_t tile,
+                                                         int32_t lo, int32_t hi, uint64_t* __restrict__ running,
+                                                         int32_t* __restrict__ run_count) {
+  constexpr int NT = 256;
+  __shared__ uint64_t s_run[K];
+  __shared__ uint32_t s_hist[256];
+  __shared__ BlockScratch<NT> s_red;
+  __shared__ int32_t s_n;
+  const int64_t row = blockIdx.x;
+  if (row_state[row] != kRowLong) return;
+  const int32_t a = max(row_start[row], lo), b = min(row_end[row], hi);
+  if (a >= b) return;
+  const int n_run = run_count[row];
+  const int n_tile = b - a;
+  uint64_t* run = running + static_cast<size_t>(row) * K;
+  for (int i = threadIdx.x; i < n_run; i += NT) s_run[i] = run[i];
+  __syncthreads();
+  const float* lg = tile_logits + static_cast<size_t>(row) * tile + (a - lo);   // position a at lg[0]
+  auto src = [&](int64_t i, uint64_t& x) -> bool {
+    if (i < n_run) x = s_run[i];
+    else x = make_key(lg[i - n_run], static_cast<uint32_t>(a + (i - n_run)));
+    return true;
+  };
+  const int64_t n = static_cast<int64_t>(n_run) + n_tile;
+  if (n <= K) {   // everything fits: append the tile's keys
+    for (int i = threadIdx.x; i < n_tile; i += NT) {
+      uint64_t x;
+      src(n_run + i, x);
+      run[n_run + i] = x;
+    }
+    if (threadIdx.x == 0) run_count[row] = static_cast<int32_t>(n);
+    return;
+  }
+  bool ok = false;
+  const uint64_t T = block_radix_select<NT, 8>(src, n, K, s_hist, s_red, &ok);
+  if (threadIdx.x == 0) s_n = 0;
+  __syncthreads();
+  if (ok) {
+    for (int64_t i = threadIdx.x; i < n; i += NT) {
+      uint64_t x;
+      src(i, x);
+      if (x >= T) {
+        const int at = atomicAdd(&s_n, 1);
+        if (at < K) run[at] = x;
+      }
+    }
+  }
+  __syncthreads();
+  // keys are unique, so exactly K keys are >= T; anything else is a selector failure
+  if (threadIdx.x == 0) run_count[row] = (ok && s_n == K) ? K : -1;
+}
+
+template <int K>
+__global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restrict__ row_state,
+                                                        const uint64_t* __restrict__ running,
+                                                        const int32_t* __restrict__ run_count,
+                                                        const int32_t* __restrict__ page_table, int64_t P_log,
+                                                        int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot,
+                                                        int32_t* __restrict__ out_count, float* __restrict__ out_score) {
+  constexpr int NT = 256;
+  __shared__ uint64_t s_sel[K];
+  const int64_t row = blockIdx.x;
+  if (row_state[row] != kRowLong) return;
+  if (run_count[row] != K) {   // a long row visits more than K positions: anything else is a failure
+    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+    return;
+  }
+  const uint64_t* run = running + static_cast<size_t>(row) * K;
+  for (int i = threadIdx.x; i < K; i += NT) s_sel[i] = run[i];
+  __syncthreads();
+  emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
+}
+
 template <int K>
 struct Geometry;
 template <>
@@ -1123,7 +1221,38 @@ hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32
                               hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta), static_cast<unsigned>(splits));
-  dense_score_kernel<<<grid, dim3(kCtaThreads), 0, st>>>(scan_args(p, row_state, splits), logits);
+  const int64_t S = p.P_log * kPage;
+  dense_score_kernel<<<grid, dim3(kCtaThreads), 0, st>>>(scan_args(p, row_state, splits), logits, S, 0,
+                                                          static_cast<int32_t>(S));
+  return hipGetLastError();
+}
+
+hipError_t launch_tiled(const PathArgs& p, const int32_t* row_state, int32_t splits, int32_t tile, float* tile_logits,
+                        uint64_t* running, int32_t* run_count, hipStream_t st) {
+  if (p.Q == 0) return hipSuccess;
+  const int64_t S = p.P_log * kPage;
+  const dim3 sgrid(static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta), static_cast<unsigned>(splits));
+  const dim3 rgrid(static_cast<unsigned>(p.Q));
+  const ScanArgs a = scan_args(p, row_state, splits);
+  tile_reset_kernel<<<dim3(static_cast<unsigned>((p.Q + 255) / 256)), dim3(256), 0, st>>>(run_count, p.Q);
+  for (int64_t lo = 0; lo < S; lo += tile) {
+    const int32_t hi = static_cast<int32_t>(lo + tile < S ? lo + tile : S);
+    dense_score_kernel<<<sgrid, dim3(kCtaThreads), 0, st>>>(a, tile_logits, tile, static_cast<int32_t>(lo), hi);
+    if (p.K == 512)
+      tile_merge_kernel<512><<<rgrid, dim3(256), 0, st>>>(row_state, p.row_start, p.row_end, tile_logits, tile,
+                                                          static_cast<int32_t>(lo), hi, running, run_count);
+    else
+      tile_merge_kernel<1024><<<rgrid, dim3(256), 0, st>>>(row_state, p.row_start, p.row_end, tile_logits, tile,
+                                                           static_cast<int32_t>(lo), hi, running, run_count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.K == 512)
+    tile_emit_kernel<512><<<rgrid, dim3(256), 0, st>>>(row_state, running, run_count, p.page_table, p.P_log,
+                                                       p.out_raw, p.out_slot, p.out_count, p.out_score);
+  else
+    tile_emit_kernel<1024><<<rgrid, dim3(256), 0, st>>>(row_state, running, run_count, p.page_table, p.P_log,
+                                                        p.out_raw, p.out_slot, p.out_count, p.out_score);
   return hipGetLastError();
 }
 

@@ -50,6 +50,10 @@ hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t 
                               hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
                               hipStream_t st);
+// Bounded context-tiled exact TopK over long rows (row_state from row_prep):
+// tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.
+hipError_t launch_tiled(const PathArgs& p, const int32_t* row_state, int32_t splits, int32_t tile, float* tile_logits,
+                        uint64_t* running, int32_t* run_count, hipStream_t st);
 hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int32_t* row_state,
                               hipStream_t st);
 // Copies the sticky status word to *host_out and clears it (synchronises st).

@@ -139,6 +139,28 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
                                    float* logits, int32_t* out_raw, int32_t* out_slot,
                                    int32_t* out_count, float* out_score, void* stream);
 
+/*
+ * Bounded context-tiled exact TopK: the correctness / reference fallback of
+ * "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK" (ROCm/aiter PR 5282),
+ * Changes. Same inputs, outputs and contract as mqa_fp4_topk_prefill (K, short
+ * rows, windows, pages, fail closed, page map), computed another way: the
+ * context is visited in tiles of tile_positions logical positions (a multiple
+ * of 256; 0 = 4096); per tile the fp32 scores of every row are written to a
+ * [Q, tile_positions] scratch buffer by the dense scorer, and every long row
+ * merges its running exact top-K with the tile's keys by exact radix select. No
+ * gate, no calibration. Outputs are identical to mqa_fp4_topk_prefill's
+ * (scores bit-identical). Stream-ordered scratch:
+ * mqa_fp4_tiled_scratch_bytes(Q, K, tile) = O(Q) + Q*K*8 + Q*tile*4 bytes,
+ * independent of the context length. Returns MQA_ERR_BAD_SIZE for a bad tile.
+ */
+int32_t mqa_fp4_tiled_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                   const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                                   const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                                   const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                   int32_t tile_positions, int32_t* out_raw, int32_t* out_slot,
+                                   int32_t* out_count, float* out_score, void* stream);
+int64_t mqa_fp4_tiled_scratch_bytes(int64_t num_rows, int32_t K, int32_t tile_positions);
+
 /* The dense path's scorer alone: logits as above, for every row with a valid
  * window and valid pages (no length condition). */
 int32_t mqa_fp4_dense_logits(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,

@@ -62,3 +62,18 @@ def dense_logits(dev):
                              dev["page_table"], dev["row_start"], dev["row_end"], logits)
     torch.cuda.synchronize()
     return logits.cpu().numpy()
+
+
+def run_tiled(dev, K, tile=0, with_score=True):
+    import torch
+    Q = dev["q"].shape[0]
+    outs = mqa.alloc_outputs(Q, K, dev["q"].device, with_score=with_score)
+    for t in outs:
+        t.fill_(-7)
+    score = outs[3] if with_score else None
+    mqa.mqa_fp4_tiled_topk_prefill(dev["q"], dev["q_scale"], dev["k_pages"], dev["k_scale"], dev["weights"],
+                                   dev["page_table"], dev["row_start"], dev["row_end"], K,
+                                   outs[0], outs[1], outs[2], score, tile_positions=tile)
+    torch.cuda.synchronize()
+    res = [t.cpu().numpy() for t in outs]
+    return res[0], res[1], res[2], (res[3] if with_score else None)

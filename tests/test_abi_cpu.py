@@ -112,3 +112,18 @@ def test_quantizer_and_cache_writer_reject_bad_arguments_on_host(lib):
     assert lib.mqa_fp4_cache_write(a, 4, a, a, -1, 1, a, a, None) == -4
     assert lib.mqa_fp4_cache_write(a, 4, None, a, 1, 1, a, a, None) == -2
     assert lib.mqa_fp4_cache_write(a, 4, a, a, 1, 1, P(0x1008), a, None) == -3
+
+
+def test_tiled_path_checks_tile_and_k_on_host(lib):
+    import fp4_mqa_scoring_amd as m
+    P = ctypes.c_void_p
+    p = P(0x1000)
+    args = (p, p, 2, p, p, 2, p, p, 2, p, p)
+    assert lib.mqa_fp4_tiled_topk_prefill(*args, 512, 300, p, p, p, None, None) == -4     # not a multiple of 256
+    assert lib.mqa_fp4_tiled_topk_prefill(*args, 512, -256, p, p, p, None, None) == -4
+    assert lib.mqa_fp4_tiled_topk_prefill(*args, 640, 256, p, p, p, None, None) == -1     # unsupported K
+    # scratch: O(Q) + Q*K*8 + Q*tile*4, no context argument at all
+    q, K, T = 1000, 1024, 4096
+    want = 2 * ((q * 4 + 255) // 256 * 256) + (q * K * 8 + 255) // 256 * 256 + (q * T * 4 + 255) // 256 * 256
+    assert m.mqa_fp4_tiled_scratch_bytes(q, K, T) == want
+    assert m.mqa_fp4_tiled_scratch_bytes(q, K, 0) == want      # 0 = the 4096 default
