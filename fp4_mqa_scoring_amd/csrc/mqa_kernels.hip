@@ -1029,8 +1029,9 @@ __global__ void __launch_bounds__(1024) logits_topk_kernel(
 // Gated candidate buffer per row, and the fallback's pool and splits.
 // ---------------------------------------------------------------------------
 // Bounded context-tiled exact TopK ("[FlyDSL][DSv4] Prototype FP4 MQA streaming
-// TopK", Changes: a bounded context-tiled implementation as the correctness /
-// reference fallback). The context is visited in tiles of `tile` positions; the
+// TopK", Changes: besides the fused operator the pages keep an exact path whose
+// memory is bounded by tiling the context, for correctness checks and as a
+// reference). The context is visited in tiles of `tile` positions; the
 // dense scorer writes one tile's fp32 scores of every row into a [Q, tile]
 // buffer, then each row merges its running exact top-K (at most K keys, same
 // total order) with the tile's keys by an exact radix select. Every position of
