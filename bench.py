@@ -44,12 +44,20 @@ PAGES_LITETOPK_MS = {  # PR 5309 Validation table, MI355X, LiteTopK column
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_kernel_traffic.json")
 
 
-def kernel_source_hash() -> str:
+def code_hash(*files: str) -> str:
+    """Hash of the code of the given csrc files (comments and whitespace removed):
+    the byte counters in profiles/ stay valid while this hash is unchanged."""
+    import re
     h = hashlib.sha256()
-    for f in ("mqa_device.h", "mqa_kernels.hip"):
-        with open(os.path.join(ROOT, "fp4_mqa_scoring_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in files:
+        with open(os.path.join(ROOT, "fp4_mqa_scoring_amd", "csrc", f)) as fh:
+            text = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_hash() -> str:
+    return code_hash("mqa_device.h", "mqa_kernels.hip")
 
 
 class HipEvents:
@@ -173,10 +181,8 @@ def bench_quantize(args, torch, mqa, dev):
     if os.path.exists(tf):
         with open(tf) as fh:
             tr = json.load(fh)
-        src = os.path.join(ROOT, "fp4_mqa_scoring_amd", "csrc", "mqa_quant.hip")
-        with open(src, "rb") as fh:
-            if tr.get("kernel_source_hash") == hashlib.sha256(fh.read()).hexdigest()[:16]:
-                traffic = tr.get("bytes_per_launch")
+        if tr.get("kernel_source_hash") == code_hash("mqa_device.h", "mqa_quant.hip"):
+            traffic = tr.get("bytes_per_launch")
     line = {
         "metric": "GB/s, MXFP4 quantisation of the query tensor + C4 cache write (headline shape)",
         "value": (q_bytes + w_bytes) / (wall_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
