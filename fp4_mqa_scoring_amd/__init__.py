@@ -70,12 +70,16 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_tiled_topk_prefill.argtypes = prefill[:11] + [i32, i32, P, P, P, P, P]
         L.mqa_fp4_tiled_scratch_bytes.argtypes = [i64, i32, i32]
         L.mqa_fp4_tiled_scratch_bytes.restype = i64
+        L.mqa_fp4_topk_decode.argtypes = [P, P, i64, P, P, i64, P, P, i64, i64, P, P, P, i32, P, P, P, P, P, i64,
+                                          i32, P]
+        L.mqa_fp4_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
+        L.mqa_fp4_decode_workspace_bytes.restype = i64
         L.mqa_fp4_cache_write.argtypes = [P, i64, P, P, i64, i64, P, P, P]
         for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
                      "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events",
                      "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write",
-                     "mqa_fp4_tiled_topk_prefill"):
+                     "mqa_fp4_tiled_topk_prefill", "mqa_fp4_topk_decode"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -213,6 +217,38 @@ def mqa_fp4_tiled_scratch_bytes(num_rows: int, K: int, tile_positions: int = 0) 
     if r < 0:
         raise MQAError(r, "mqa_fp4_tiled_scratch_bytes")
     return r
+
+
+def mqa_fp4_decode_workspace_bytes(num_rows: int, K: int, splits: int = 0, device: int = 0) -> int:
+    r = int(lib().mqa_fp4_decode_workspace_bytes(int(num_rows), int(K), int(splits), int(device)))
+    if r < 0:
+        raise MQAError(r, "mqa_fp4_decode_workspace_bytes")
+    return r
+
+
+def mqa_fp4_topk_decode(q, q_scale, k_pages, k_scale, weights, block_table, seq_of_row, row_start, row_end, K,
+                        out_raw, out_slot, out_count, workspace, out_score=None, splits=0, stream=None):
+    """Decode / multi-sequence form: block_table int32 [n_seq, max_pages], seq_of_row int32 [Q],
+    workspace a uint8 device tensor of at least mqa_fp4_decode_workspace_bytes(Q, K, splits) bytes.
+    Allocates nothing and does not synchronise (capturable)."""
+    import torch
+    _check(q, "q", torch.uint8, 3)
+    _check(q_scale, "q_scale", torch.uint8, 3)
+    _check(k_pages, "k_pages", torch.uint8, 3)
+    _check(k_scale, "k_scale", torch.uint8, 3)
+    _check(weights, "weights", torch.float32, 2)
+    _check(block_table, "block_table", torch.int32, 2)
+    for t, n in ((seq_of_row, "seq_of_row"), (row_start, "row_start"), (row_end, "row_end")):
+        _check(t, n, torch.int32, 1)
+    _check(workspace, "workspace", torch.uint8)
+    Q = q.shape[0]
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    rc = lib().mqa_fp4_topk_decode(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), k_pages.shape[0], _ptr(weights),
+        _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(seq_of_row), _ptr(row_start),
+        _ptr(row_end), int(K), _ptr(out_raw), _ptr(out_slot), _ptr(out_count), _ptr(out_score), _ptr(workspace),
+        workspace.numel(), int(splits), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_topk_decode")
 
 
 def mqa_fp4_dense_logits(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, logits,

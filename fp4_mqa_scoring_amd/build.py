@@ -8,7 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmqa_fp4.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mqa_kernels.hip", "mqa_api.hip", "mqa_probe.hip", "mqa_quant.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mqa_kernels.hip", "mqa_api.hip", "mqa_probe.hip", "mqa_quant.hip", "mqa_decode.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

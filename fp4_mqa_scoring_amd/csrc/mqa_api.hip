@@ -168,14 +168,17 @@ FusedScratch fused_scratch_layout(int64_t Q, int32_t K) {
 
 // Common entry checks; on success the guard holds the tensors' device.
 // Order: host-only checks first (testable without a GPU), then device checks.
-int32_t enter(hipStream_t st, const PtrSpec* specs, int nspecs, DeviceGuard& guard, DeviceInfo* info) {
+int32_t enter(hipStream_t st, const PtrSpec* specs, int nspecs, DeviceGuard& guard, DeviceInfo* info,
+              bool allow_capture = false) {
   int32_t rc = check_ptrs_host(specs, nspecs);
   if (rc != MQA_OK) return rc;
   int dev = -1;
   rc = stream_device(st, &dev);
   if (rc != MQA_OK) return rc;
-  rc = check_capture(st);
-  if (rc != MQA_OK) return rc;
+  if (!allow_capture) {
+    rc = check_capture(st);
+    if (rc != MQA_OK) return rc;
+  }
   rc = device_info(dev, info);
   if (rc != MQA_OK) return rc;
   rc = check_ptrs_device(specs, nspecs, dev);
@@ -484,6 +487,67 @@ int64_t mqa_fp4_tiled_scratch_bytes(int64_t num_rows, int32_t K, int32_t tile_po
   return static_cast<int64_t>(2 * align_up(Qz * sizeof(int32_t)) +
                               align_up(Qz * static_cast<size_t>(K) * sizeof(uint64_t)) +
                               align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float)));
+}
+
+// Context splits of the decode path: enough (row, split) waves for two
+// 4-wave CTAs per CU.
+static int32_t decode_splits(int64_t Q, int cus, int32_t requested) {
+  if (requested > 0) return requested;
+  const int64_t target = 8ll * cus;
+  int64_t s = (target + Q - 1) / (Q > 0 ? Q : 1);
+  if (s < 1) s = 1;
+  if (s > mqa::kMaxDecodeSplits) s = mqa::kMaxDecodeSplits;
+  return static_cast<int32_t>(s);
+}
+
+int64_t mqa_fp4_decode_workspace_bytes(int64_t num_rows, int32_t K, int32_t splits, int32_t device) {
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (num_rows < 0 || num_rows > 0x7FFFFFFFll || splits < 0 || splits > mqa::kMaxDecodeSplits)
+    return MQA_ERR_BAD_SIZE;
+  int cus = 256;
+  if (splits == 0) {
+    DeviceInfo info;
+    const int32_t rc = device_info(device, &info);
+    if (rc != MQA_OK) return rc;
+    cus = info.cus;
+  }
+  return static_cast<int64_t>(mqa::decode_scratch_bytes(num_rows, K, decode_splits(num_rows, cus, splits)));
+}
+
+int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows, const uint8_t* k_pages,
+                            const uint8_t* k_scale, int64_t num_phys_pages, const float* weights,
+                            const int32_t* block_table, int64_t num_seqs, int64_t max_pages,
+                            const int32_t* seq_of_row, const int32_t* row_start, const int32_t* row_end, int32_t K,
+                            int32_t* out_raw, int32_t* out_slot, int32_t* out_count, float* out_score,
+                            void* workspace, int64_t workspace_bytes, int32_t splits, void* stream) {
+  if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  int32_t rc = check_sizes(num_rows, num_phys_pages, max_pages);
+  if (rc != MQA_OK) return rc;
+  if (num_seqs < 0 || (max_pages > 0 && num_seqs > 0x7FFFFFFFll / max_pages)) return MQA_ERR_BAD_SIZE;
+  if (splits < 0 || splits > mqa::kMaxDecodeSplits || workspace_bytes < 0) return MQA_ERR_BAD_SIZE;
+  const bool rows = num_rows > 0;
+  const PtrSpec specs[] = {
+      {q, rows, 16},          {q_scale, rows, 4},     {k_pages, num_phys_pages > 0, 16},
+      {k_scale, num_phys_pages > 0, 16}, {weights, rows, 4}, {block_table, num_seqs > 0 && max_pages > 0, 4},
+      {seq_of_row, rows, 4},  {row_start, rows, 4},   {row_end, rows, 4},
+      {out_raw, rows, 4},     {out_slot, rows, 4},    {out_count, rows, 4},
+      {out_score, false, 4},  {workspace, rows, 256},
+  };
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  DeviceGuard guard;
+  DeviceInfo info;
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info, /*allow_capture=*/true);
+  if (rc != MQA_OK || !rows) return rc;
+  const int32_t sp = decode_splits(num_rows, info.cus, splits);
+  if (static_cast<size_t>(workspace_bytes) < mqa::decode_scratch_bytes(num_rows, K, sp)) return MQA_ERR_BAD_SIZE;
+  PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  block_table,
+             max_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  p.seq_of_row = seq_of_row;
+  p.n_seq = num_seqs;
+  const mqa::DecodeScratch w = mqa::decode_scratch_layout(workspace, num_rows, K, sp);
+  rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, nullptr, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, st));
+  return rc;
 }
 
 int32_t mqa_fp4_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t* scales, void* stream) {

@@ -26,6 +26,7 @@
 // (ROCm/aiter PR 5282), Changes and Scope.
 #include "mqa_device.h"
 #include "mqa_launch.h"
+#include "mqa_select.h"
 
 #include <climits>
 
@@ -42,17 +43,23 @@ __device__ int32_t g_status;
 // mode 1 (logits only): every valid non-empty row -> kRowLong, no outputs.
 // Block 0 also clears the fallback list counter of this call (if any).
 // ---------------------------------------------------------------------------
+// With seq_of_row (multi-sequence form) row r reads the page table
+// page_table + seq_of_row[r] * P_log; a sequence index outside [0, n_seq) is
+// invalid metadata (code -1).
 __global__ void __launch_bounds__(256) row_prep_kernel(
     const int32_t* __restrict__ row_start, const int32_t* __restrict__ row_end,
-    const int32_t* __restrict__ page_table, int64_t P_log, int64_t P_phys, int32_t K, int mode,
+    const int32_t* __restrict__ page_table_base, int64_t P_log, int64_t P_phys, int32_t K, int mode,
     int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
-    float* __restrict__ out_score, int32_t* __restrict__ row_state, int32_t* __restrict__ fb_count) {
+    float* __restrict__ out_score, int32_t* __restrict__ row_state, int32_t* __restrict__ fb_count,
+    const int32_t* __restrict__ seq_of_row, int64_t n_seq) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   if (row == 0 && tid == 0 && fb_count) *fb_count = 0;
   const int64_t start = row_start[row], end = row_end[row];
+  const int64_t seq = seq_of_row ? seq_of_row[row] : 0;
+  const int32_t* page_table = page_table_base + (seq_of_row && seq >= 0 && seq < n_seq ? seq * P_log : 0);
   int code = 0;
-  if (start < 0 || end < start || end > kPage * P_log) {
+  if (start < 0 || end < start || end > kPage * P_log || (seq_of_row && (seq < 0 || seq >= n_seq))) {
     code = kCodeBadWindow;
   } else if (end > start) {
     const int64_t p0 = start / kPage, p1 = (end - 1) / kPage;
@@ -624,204 +631,6 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Block-level exact radix select (256 or 1024 threads) over unique 64-bit keys
-// produced by a source functor: src(i, &key) -> bool (valid), i in [0, n).
-// Digits of DBITS bits, starting at the highest bit where the valid keys differ.
-// Returns T with exactly k valid keys >= T (k <= number of valid keys), or
-// sets *ok = false if the keys break the invariants.
-// ---------------------------------------------------------------------------
-template <int NT>
-struct BlockScratch {
-  uint64_t red64[2][NT / 64];
-  uint32_t red32[NT / 64];
-  int32_t redi[NT / 64];
-  uint32_t wtot[NT / 64];
-};
-
-template <int NT>
-__device__ __forceinline__ void block_or_and(uint64_t& vor, uint64_t& vand, BlockScratch<NT>& s) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  vor = wave_or64(vor);
-  vand = wave_and64(vand);
-  if (lane == 0) {
-    s.red64[0][w] = vor;
-    s.red64[1][w] = vand;
-  }
-  __syncthreads();
-  vor = 0;
-  vand = ~0ull;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    vor |= s.red64[0][i];
-    vand &= s.red64[1][i];
-  }
-  __syncthreads();
-}
-
-template <int NT>
-__device__ __forceinline__ int block_max_i32(int v, BlockScratch<NT>& s) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_max_i32(v);
-  if (lane == 0) s.redi[w] = v;
-  __syncthreads();
-  int r = INT_MIN;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) r = max(r, s.redi[i]);
-  __syncthreads();
-  return r;
-}
-
-// Inclusive suffix sum over the NT threads (thread order).
-template <int NT>
-__device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, BlockScratch<NT>& s) {
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_suffix_sum(v, lane);
-  if (lane == 0) s.wtot[w] = v;
-  __syncthreads();
-  uint32_t add = 0;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i)
-    if (i > w) add += s.wtot[i];
-  __syncthreads();
-  return v + add;
-}
-
-template <int NT, int DBITS, class Src>
-__device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_t* hist,
-                                       BlockScratch<NT>& s, bool* ok) {
-  constexpr int BINS = 1 << DBITS;
-  constexpr int BPT = BINS / NT;  // bins per thread
-  static_assert(BPT >= 1 && BINS % NT == 0, "bins must be a multiple of threads");
-  const int tid = threadIdx.x;
-  uint64_t vor = 0, vand = ~0ull;
-  for (int64_t i = tid; i < n; i += NT) {
-    uint64_t x;
-    if (src(i, x)) {
-      vor |= x;
-      vand &= x;
-    }
-  }
-  block_or_and<NT>(vor, vand, s);
-  if (vor == vand) {   // at most one distinct valid key
-    *ok = (k == 1);
-    return vand;
-  }
-  int hb = 63 - __clzll(static_cast<long long>(vor ^ vand));
-  uint64_t pmask = ~((2ull << hb) - 1ull);
-  uint64_t prefix = vand & pmask;
-  uint32_t krem = static_cast<uint32_t>(k);
-  for (;;) {
-    const int shift = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;
-    for (int b = tid; b < BINS; b += NT) hist[b] = 0u;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += NT) {
-      uint64_t x;
-      if (src(i, x) && (x & pmask) == prefix)
-        atomicAdd(&hist[static_cast<uint32_t>(x >> shift) & (BINS - 1)], 1u);
-    }
-    __syncthreads();
-    uint32_t c[BPT];
-    uint32_t tsum = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      c[j] = hist[tid * BPT + j];
-      tsum += c[j];
-    }
-    const uint32_t incl = block_suffix_sum<NT>(tsum, s);
-    uint32_t suf = incl - tsum;   // suffix strictly after this thread's bins
-    int local = -1;
-    uint32_t local_suffix = 0;
-#pragma unroll
-    for (int j = BPT - 1; j >= 0; --j) {
-      suf += c[j];
-      if (suf >= krem && local < 0) {
-        local = tid * BPT + j;
-        local_suffix = suf;
-      }
-    }
-    const int dstar = block_max_i32<NT>(local, s);
-    if (dstar < 0) {
-      *ok = false;
-      return prefix;
-    }
-    if (local == dstar) s.red32[0] = local_suffix;
-    __syncthreads();
-    const uint32_t suffix_d = s.red32[0];
-    const uint32_t cnt_d = hist[dstar];
-    __syncthreads();
-    krem -= suffix_d - cnt_d;
-    prefix |= static_cast<uint64_t>(dstar) << shift;
-    pmask |= static_cast<uint64_t>(BINS - 1) << shift;
-    if (cnt_d == krem || shift == 0) break;
-    hb = shift - 1;
-  }
-  *ok = true;
-  return prefix;
-}
-
-// Sorts N (power of two) 64-bit values ascending in LDS with NT threads.
-template <int N, int NT>
-__device__ __forceinline__ void block_bitonic_sort(uint64_t* v) {
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < N / 2; i += NT) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t x = v[lo], y = v[hi];
-        if ((x > y) == up) {
-          v[lo] = y;
-          v[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// Writes one long row's K selected keys (in s_sel) in ascending position order
-// with their physical slots. s_sel is overwritten.
-template <int K, int NT>
-__device__ __forceinline__ void emit_row(uint64_t* s_sel, int64_t row, const int32_t* __restrict__ page_table,
-                                         int64_t P_log, int32_t* __restrict__ out_raw,
-                                         int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
-                                         float* __restrict__ out_score) {
-  for (int i = threadIdx.x; i < K; i += NT) {
-    const uint64_t key = s_sel[i];
-    s_sel[i] = (static_cast<uint64_t>(key_pos(key)) << 32) | static_cast<uint32_t>(key >> 32);
-  }
-  __syncthreads();
-  block_bitonic_sort<K, NT>(s_sel);
-  const size_t base = static_cast<size_t>(row) * K;
-  for (int i = threadIdx.x; i < K; i += NT) {
-    const uint64_t v = s_sel[i];
-    const uint32_t pos = static_cast<uint32_t>(v >> 32);
-    const int64_t lp = pos / kPage;   // always < P_log for keys of validated windows
-    out_raw[base + i] = static_cast<int32_t>(pos);
-    out_slot[base + i] = lp < P_log ? static_cast<int32_t>(static_cast<int64_t>(page_table[lp]) * kPage + pos % kPage)
-                                    : -1;
-    if (out_score) out_score[base + i] = key_score(static_cast<uint64_t>(static_cast<uint32_t>(v)) << 32);
-  }
-  if (threadIdx.x == 0) out_count[row] = K;
-}
-
-template <int K, int NT>
-__device__ __forceinline__ void fail_row(int64_t row, int code, int32_t* __restrict__ out_raw,
-                                         int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
-                                         float* __restrict__ out_score) {
-  const size_t base = static_cast<size_t>(row) * K;
-  for (int i = threadIdx.x; i < K; i += NT) {
-    out_raw[base + i] = -1;
-    out_slot[base + i] = -1;
-    if (out_score) out_score[base + i] = __uint_as_float(0x7FC00000u);
-  }
-  if (threadIdx.x == 0) {
-    out_count[row] = code;
-    atomicOr(&g_status, code == kCodeUnderfill ? kStUnderfill : kStSelector);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Exact merge of the gated candidates + page mapping + emission. One 256-thread
 // CTA per long row. The candidates are all of the window's keys above the gate;
 // with at least K of them the row's top-K is among them ("exact candidate
@@ -869,7 +678,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ 
     }
     __syncthreads();
     if (!ok || s_n != K) {
-      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
       return;
     }
   }
@@ -907,7 +716,7 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
     }
     __syncthreads();
     if (s_total < K) {
-      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
       __syncthreads();
       continue;
     }
@@ -931,7 +740,7 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
     }
     __syncthreads();
     if (!ok || s_n != K) {
-      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
     } else {
       emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
     }
@@ -1020,7 +829,7 @@ __global__ void __launch_bounds__(1024) logits_topk_kernel(
   }
   __syncthreads();
   if (!ok || s_n != K) {
-    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
     return;
   }
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
@@ -1112,7 +921,7 @@ __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restric
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
   if (run_count[row] != K) {   // a long row visits more than K positions: anything else is a failure
-    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score);
+    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
     return;
   }
   const uint64_t* run = running + static_cast<size_t>(row) * K;
@@ -1178,7 +987,7 @@ hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int3
   if (p.Q == 0) return hipSuccess;
   row_prep_kernel<<<dim3(static_cast<unsigned>(p.Q)), dim3(256), 0, st>>>(
       p.row_start, p.row_end, p.page_table, p.P_log, p.P_phys, p.K, mode, p.out_raw, p.out_slot,
-      p.out_count, p.out_score, row_state, fb_count);
+      p.out_count, p.out_score, row_state, fb_count, p.seq_of_row, p.n_seq);
   return hipGetLastError();
 }
 
@@ -1273,12 +1082,23 @@ hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int3
   return hipGetLastError();
 }
 
+// Cached per device after the first lookup (the address is fixed for the
+// process), so that calls made while a stream is being captured do no lookups.
 int32_t* status_word() {
+  constexpr int kMaxDevices = 64;
+  static int32_t* cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (dev < kMaxDevices && cache[dev] != nullptr) return cache[dev];
   void* p = nullptr;
   if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_status)) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
+  if (dev < kMaxDevices) cache[dev] = static_cast<int32_t*>(p);
   return static_cast<int32_t*>(p);
 }
 

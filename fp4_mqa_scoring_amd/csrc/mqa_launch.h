@@ -24,6 +24,10 @@ struct PathArgs {
   int32_t* out_slot;
   int32_t* out_count;
   float* out_score;
+  // Multi-sequence form (nullptr = one page table for every row): row r uses
+  // the page table page_table + seq_of_row[r] * P_log of n_seq tables.
+  const int32_t* seq_of_row = nullptr;
+  int64_t n_seq = 0;
 };
 
 // Scratch of the gated fused path (one call).
@@ -50,6 +54,18 @@ hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t 
                               hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
                               hipStream_t st);
+// Decode / multi-sequence path: per-wave streaming exact TopK over each row's
+// own pages, then an exact merge of the splits. Scratch comes from the caller.
+struct DecodeScratch {
+  int32_t* row_state;   // [Q]
+  int32_t* counts;      // [Q, splits]
+  uint64_t* keys;       // [Q, splits, K]
+};
+constexpr int kMaxDecodeSplits = 64;
+size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
+DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, hipStream_t st);
+
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.
 hipError_t launch_tiled(const PathArgs& p, const int32_t* row_state, int32_t splits, int32_t tile, float* tile_logits,

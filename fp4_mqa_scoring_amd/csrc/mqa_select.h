@@ -1,0 +1,209 @@
+// Block-level selection helpers (exact radix select over unique 64-bit keys,
+// bitonic sort, row emission with the page map) shared by the kernels of the
+// fused, dense, tiled and decode paths.
+#pragma once
+
+#include "mqa_device.h"
+
+namespace mqa {
+
+// ---------------------------------------------------------------------------
+// Block-level exact radix select (256 or 1024 threads) over unique 64-bit keys
+// produced by a source functor: src(i, &key) -> bool (valid), i in [0, n).
+// Digits of DBITS bits, starting at the highest bit where the valid keys differ.
+// Returns T with exactly k valid keys >= T (k <= number of valid keys), or
+// sets *ok = false if the keys break the invariants.
+// ---------------------------------------------------------------------------
+template <int NT>
+struct BlockScratch {
+  uint64_t red64[2][NT / 64];
+  uint32_t red32[NT / 64];
+  int32_t redi[NT / 64];
+  uint32_t wtot[NT / 64];
+};
+
+template <int NT>
+__device__ __forceinline__ void block_or_and(uint64_t& vor, uint64_t& vand, BlockScratch<NT>& s) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  vor = wave_or64(vor);
+  vand = wave_and64(vand);
+  if (lane == 0) {
+    s.red64[0][w] = vor;
+    s.red64[1][w] = vand;
+  }
+  __syncthreads();
+  vor = 0;
+  vand = ~0ull;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    vor |= s.red64[0][i];
+    vand &= s.red64[1][i];
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ int block_max_i32(int v, BlockScratch<NT>& s) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = wave_max_i32(v);
+  if (lane == 0) s.redi[w] = v;
+  __syncthreads();
+  int r = INT_MIN;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = max(r, s.redi[i]);
+  __syncthreads();
+  return r;
+}
+
+// Inclusive suffix sum over the NT threads (thread order).
+template <int NT>
+__device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, BlockScratch<NT>& s) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = wave_suffix_sum(v, lane);
+  if (lane == 0) s.wtot[w] = v;
+  __syncthreads();
+  uint32_t add = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i)
+    if (i > w) add += s.wtot[i];
+  __syncthreads();
+  return v + add;
+}
+
+template <int NT, int DBITS, class Src>
+__device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_t* hist,
+                                       BlockScratch<NT>& s, bool* ok) {
+  constexpr int BINS = 1 << DBITS;
+  constexpr int BPT = BINS / NT;  // bins per thread
+  static_assert(BPT >= 1 && BINS % NT == 0, "bins must be a multiple of threads");
+  const int tid = threadIdx.x;
+  uint64_t vor = 0, vand = ~0ull;
+  for (int64_t i = tid; i < n; i += NT) {
+    uint64_t x;
+    if (src(i, x)) {
+      vor |= x;
+      vand &= x;
+    }
+  }
+  block_or_and<NT>(vor, vand, s);
+  if (vor == vand) {   // at most one distinct valid key
+    *ok = (k == 1);
+    return vand;
+  }
+  int hb = 63 - __clzll(static_cast<long long>(vor ^ vand));
+  uint64_t pmask = ~((2ull << hb) - 1ull);
+  uint64_t prefix = vand & pmask;
+  uint32_t krem = static_cast<uint32_t>(k);
+  for (;;) {
+    const int shift = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;
+    for (int b = tid; b < BINS; b += NT) hist[b] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += NT) {
+      uint64_t x;
+      if (src(i, x) && (x & pmask) == prefix)
+        atomicAdd(&hist[static_cast<uint32_t>(x >> shift) & (BINS - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t c[BPT];
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      c[j] = hist[tid * BPT + j];
+      tsum += c[j];
+    }
+    const uint32_t incl = block_suffix_sum<NT>(tsum, s);
+    uint32_t suf = incl - tsum;   // suffix strictly after this thread's bins
+    int local = -1;
+    uint32_t local_suffix = 0;
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      suf += c[j];
+      if (suf >= krem && local < 0) {
+        local = tid * BPT + j;
+        local_suffix = suf;
+      }
+    }
+    const int dstar = block_max_i32<NT>(local, s);
+    if (dstar < 0) {
+      *ok = false;
+      return prefix;
+    }
+    if (local == dstar) s.red32[0] = local_suffix;
+    __syncthreads();
+    const uint32_t suffix_d = s.red32[0];
+    const uint32_t cnt_d = hist[dstar];
+    __syncthreads();
+    krem -= suffix_d - cnt_d;
+    prefix |= static_cast<uint64_t>(dstar) << shift;
+    pmask |= static_cast<uint64_t>(BINS - 1) << shift;
+    if (cnt_d == krem || shift == 0) break;
+    hb = shift - 1;
+  }
+  *ok = true;
+  return prefix;
+}
+
+// Sorts N (power of two) 64-bit values ascending in LDS with NT threads.
+template <int N, int NT>
+__device__ __forceinline__ void block_bitonic_sort(uint64_t* v) {
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < N / 2; i += NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = v[lo], y = v[hi];
+        if ((x > y) == up) {
+          v[lo] = y;
+          v[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Writes one long row's K selected keys (in s_sel) in ascending position order
+// with their physical slots. s_sel is overwritten.
+template <int K, int NT>
+__device__ __forceinline__ void emit_row(uint64_t* s_sel, int64_t row, const int32_t* __restrict__ page_table,
+                                         int64_t P_log, int32_t* __restrict__ out_raw,
+                                         int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
+                                         float* __restrict__ out_score) {
+  for (int i = threadIdx.x; i < K; i += NT) {
+    const uint64_t key = s_sel[i];
+    s_sel[i] = (static_cast<uint64_t>(key_pos(key)) << 32) | static_cast<uint32_t>(key >> 32);
+  }
+  __syncthreads();
+  block_bitonic_sort<K, NT>(s_sel);
+  const size_t base = static_cast<size_t>(row) * K;
+  for (int i = threadIdx.x; i < K; i += NT) {
+    const uint64_t v = s_sel[i];
+    const uint32_t pos = static_cast<uint32_t>(v >> 32);
+    const int64_t lp = pos / kPage;   // always < P_log for keys of validated windows
+    out_raw[base + i] = static_cast<int32_t>(pos);
+    out_slot[base + i] = lp < P_log ? static_cast<int32_t>(static_cast<int64_t>(page_table[lp]) * kPage + pos % kPage)
+                                    : -1;
+    if (out_score) out_score[base + i] = key_score(static_cast<uint64_t>(static_cast<uint32_t>(v)) << 32);
+  }
+  if (threadIdx.x == 0) out_count[row] = K;
+}
+
+template <int K, int NT>
+__device__ __forceinline__ void fail_row(int64_t row, int code, int32_t* __restrict__ out_raw,
+                                         int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count,
+                                         float* __restrict__ out_score, int32_t* status) {
+  const size_t base = static_cast<size_t>(row) * K;
+  for (int i = threadIdx.x; i < K; i += NT) {
+    out_raw[base + i] = -1;
+    out_slot[base + i] = -1;
+    if (out_score) out_score[base + i] = __uint_as_float(0x7FC00000u);
+  }
+  if (threadIdx.x == 0) {
+    out_count[row] = code;
+    atomicOr(status, code == kCodeUnderfill ? kStUnderfill : kStSelector);
+  }
+}
+
+
+}  // namespace mqa

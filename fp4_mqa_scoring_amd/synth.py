@@ -221,3 +221,73 @@ def sample_rows(inp: Inputs, n: int, seed: int) -> np.ndarray:
     while len(chosen) < min(n, Q):
         chosen.add(int(rng.integers(0, Q)))
     return np.array(sorted(chosen), dtype=np.int64)
+
+
+# --- decode / multi-sequence workloads ---------------------------------------------
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """Several sequences in one shared physical page pool. Row r belongs to
+    sequence seq_of_row[r]; its window is in that sequence's logical positions;
+    block_table[s, p] is the physical page of logical page p of sequence s
+    (-1 past the sequence's pages)."""
+    q: np.ndarray
+    q_scale: np.ndarray
+    k_pages: np.ndarray
+    k_scale: np.ndarray
+    weights: np.ndarray
+    block_table: np.ndarray
+    seq_of_row: np.ndarray
+    row_start: np.ndarray
+    row_end: np.ndarray
+    seq_len: np.ndarray
+    K: int
+    name: str = ""
+
+    @property
+    def Q(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.block_table.shape[1])
+
+    def lengths(self) -> np.ndarray:
+        return self.row_end.astype(np.int64) - self.row_start.astype(np.int64)
+
+    def scored_pairs(self) -> int:
+        n = self.lengths()
+        return int(n[n > self.K].sum())
+
+    def view(self, seq: int) -> Inputs:
+        """The single-table view of one sequence (every row shares its page table)."""
+        return Inputs(self.q, self.q_scale, self.k_pages, self.k_scale, self.weights,
+                      np.ascontiguousarray(self.block_table[seq]), self.row_start, self.row_end, self.K,
+                      name=f"{self.name} seq {seq}")
+
+
+def make_decode_inputs(n_seq: int, rows_per_seq: int, min_len: int, max_len: int, K: int, seed: int, *,
+                       spare_pages: int = 3, dup_frac: float = 0.05, name: str = "") -> DecodeInputs:
+    """Seeded decode-shaped inputs: n_seq sequences with C4 lengths uniform in
+    [min_len, max_len], their pages scattered over one shuffled physical pool,
+    rows_per_seq query rows per sequence with causal windows ending at the
+    sequence's last positions (row j of a sequence: [0, len - (rows_per_seq-1-j)))."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(min_len, max_len + 1, n_seq)
+    pages = (lens + PAGE - 1) // PAGE
+    max_pages = int(pages.max())
+    P_phys = int(pages.sum()) + spare_pages
+    phys = rng.permutation(P_phys).astype(np.int32)
+    block_table = np.full((n_seq, max_pages), -1, np.int32)
+    at = 0
+    for s in range(n_seq):
+        block_table[s, :pages[s]] = phys[at:at + pages[s]]
+        at += pages[s]
+    Q = n_seq * rows_per_seq
+    base = make_inputs(Q, PAGE * P_phys, K, seed + 1, dup_frac=dup_frac, P_phys=P_phys)
+    seq_of_row = np.repeat(np.arange(n_seq, dtype=np.int32), rows_per_seq)
+    j = np.tile(np.arange(rows_per_seq), n_seq)
+    row_end = (lens[seq_of_row] - (rows_per_seq - 1 - j)).clip(min=0).astype(np.int32)
+    row_start = np.zeros(Q, np.int32)
+    return DecodeInputs(base.q, base.q_scale, base.k_pages, base.k_scale, base.weights, block_table, seq_of_row,
+                        row_start, row_end, lens.astype(np.int64), K, name=name)

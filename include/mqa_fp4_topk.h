@@ -204,6 +204,38 @@ int32_t mqa_fp4_status(void* stream, int32_t* status);
 int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
 
 /*
+ * Decode / multi-sequence form, capturable into a HIP graph. Every row has its
+ * own page table: row r belongs to sequence seq_of_row[r] and reads logical page
+ * p through block_table[seq_of_row[r] * max_pages + p]; windows, K, the short-row
+ * rule, the total order and the outputs are those of mqa_fp4_topk_prefill, with
+ * slots block_table[seq][s / 64] * 64 + s % 64 ("[FlyDSL][DSv4] Prototype FP4 MQA
+ * streaming TopK", Changes and Scope; decode is the adjacent shape that
+ * "[AMD][DSv4] Add experimental AITER FP4 streaming TopK" keeps on the older
+ * path, and graph capture the support PR 5282's Scope defers).
+ *   block_table int32 [num_seqs, max_pages]   64 * max_pages <= INT32_MAX
+ *   seq_of_row  int32 [Q]                     a row whose sequence is outside
+ *                                             [0, num_seqs) fails with code -1
+ *   workspace   device memory of at least mqa_fp4_decode_workspace_bytes(Q, K,
+ *               splits, device) bytes, 256-byte aligned, owned by the caller;
+ *               its contents need no initialisation and are scratch only
+ *   splits      context splits per row (1..64), 0 = automatic for the device
+ * The call allocates nothing, never synchronises and accepts a capturing
+ * stream; row failures are reported in out_count and the sticky status word
+ * only (read mqa_fp4_status outside the graph). Each row is scanned
+ * independently (no key sharing between rows): one wave per (row, split)
+ * streams the row's pages through a bounded LDS pool with exact radix
+ * compaction, then the splits are merged exactly. Two calls that share a
+ * workspace must be ordered (same stream).
+ */
+int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows, const uint8_t* k_pages,
+                            const uint8_t* k_scale, int64_t num_phys_pages, const float* weights,
+                            const int32_t* block_table, int64_t num_seqs, int64_t max_pages,
+                            const int32_t* seq_of_row, const int32_t* row_start, const int32_t* row_end, int32_t K,
+                            int32_t* out_raw, int32_t* out_slot, int32_t* out_count, float* out_score,
+                            void* workspace, int64_t workspace_bytes, int32_t splits, void* stream);
+int64_t mqa_fp4_decode_workspace_bytes(int64_t num_rows, int32_t K, int32_t splits, int32_t device);
+
+/*
  * MXFP4 quantisation: the producer of the FP4 inputs above. Source: the
  * payload named in "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK" (ROCm/aiter
  * PR 5282), Scope (FP4 E2M1 with UE8M0 scales); the conversion rule is the OCP

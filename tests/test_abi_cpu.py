@@ -127,3 +127,23 @@ def test_tiled_path_checks_tile_and_k_on_host(lib):
     want = 2 * ((q * 4 + 255) // 256 * 256) + (q * K * 8 + 255) // 256 * 256 + (q * T * 4 + 255) // 256 * 256
     assert m.mqa_fp4_tiled_scratch_bytes(q, K, T) == want
     assert m.mqa_fp4_tiled_scratch_bytes(q, K, 0) == want      # 0 = the 4096 default
+
+
+def test_decode_entry_checks_arguments_on_host(lib):
+    import fp4_mqa_scoring_amd as m
+    P = ctypes.c_void_p
+    p = P(0x1000)
+
+    def call(K=512, splits=0, ws=p, ws_bytes=1 << 20):
+        return lib.mqa_fp4_topk_decode(p, p, 2, p, p, 4, p, p, 2, 4, p, p, p, K, p, p, p, None, ws, ws_bytes,
+                                       splits, None)
+    assert call(K=100) == -1
+    assert call(splits=65) == -4
+    assert call(splits=-1) == -4
+    assert call(ws_bytes=-1) == -4
+    assert call(ws=None) == -2
+    assert call(ws=P(0x1010)) == -3                  # workspace needs 256-byte alignment
+    # explicit splits: no device query; O(Q) + Q*splits*(4 + 8K) bytes
+    q, K, s = 100, 1024, 5
+    a = lambda x: (x + 255) // 256 * 256
+    assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == a(q * 4) + a(q * s * 4) + a(q * s * K * 8)

@@ -1,0 +1,171 @@
+"""Decode / multi-sequence form: per-row page tables, caller workspace, graph
+capture. Checked against the oracle row by row through each sequence's own page
+table (the oracle's definition is per row), against the prefill path when all
+rows share one table, and across HIP graph replays. Bar as for the operator:
+slots, counts, padding bit-exact; scores within 1e-5; selections by
+oracle/check.py."""
+import numpy as np
+import pytest
+
+import fp4_mqa_scoring_amd as mqa
+from fp4_mqa_scoring_amd import synth
+import gpu_util as gu
+from test_gpu_parity import check_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not gu.has_gpu():
+        pytest.skip("no GPU")
+
+
+def _dev(d):
+    import torch
+    return {n: torch.from_numpy(np.ascontiguousarray(getattr(d, n))).cuda()
+            for n in ("q", "q_scale", "k_pages", "k_scale", "weights", "block_table", "seq_of_row", "row_start",
+                      "row_end")}
+
+
+def run_decode(t, K, splits=0, with_score=True):
+    import torch
+    Q = t["q"].shape[0]
+    outs = mqa.alloc_outputs(Q, K, t["q"].device, with_score=with_score)
+    for o in outs:
+        o.fill_(-7)
+    ws = torch.empty(mqa.mqa_fp4_decode_workspace_bytes(Q, K, splits), dtype=torch.uint8, device="cuda")
+    mqa.mqa_fp4_topk_decode(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], t["block_table"],
+                            t["seq_of_row"], t["row_start"], t["row_end"], K, outs[0], outs[1], outs[2], ws,
+                            out_score=outs[3] if with_score else None, splits=splits)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def check_decode(d, res, rows=None, where=""):
+    rows = range(d.Q) if rows is None else rows
+    for r in rows:
+        check_rows(d.view(int(d.seq_of_row[r])), [r], *res, where=f"{where} seq {d.seq_of_row[r]}")
+
+
+@pytest.mark.parametrize("K,rps", [(512, 1), (1024, 3)])
+def test_multi_sequence_rows_match_the_oracle(K, rps):
+    _need_gpu()
+    d = synth.make_decode_inputs(10, rps, K // 2, 9000, K, seed=40 + rps)
+    d.q[1] = 0                                             # all-equal scores in one row
+    res = run_decode(_dev(d), K)
+    check_decode(d, res, where=f"decode K={K}")
+    assert mqa.mqa_fp4_status() == 0
+
+
+def test_splits_do_not_change_outputs():
+    _need_gpu()
+    d = synth.make_decode_inputs(5, 2, 2000, 12000, 1024, seed=7)
+    t = _dev(d)
+    base = run_decode(t, 1024, splits=1)
+    for s in (3, 7, 64):
+        got = run_decode(t, 1024, splits=s)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), s
+
+
+def test_one_sequence_equals_the_prefill_path():
+    """All rows in one sequence: identical to mqa_fp4_topk_prefill bit for bit."""
+    _need_gpu()
+    import torch
+    from test_gpu_parity import medium_inputs
+    inp = medium_inputs(seed=88, K=512)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, inp.K)
+    t = {"q": dev["q"], "q_scale": dev["q_scale"], "k_pages": dev["k_pages"], "k_scale": dev["k_scale"],
+         "weights": dev["weights"], "block_table": dev["page_table"][None, :].contiguous(),
+         "seq_of_row": torch.zeros(inp.Q, dtype=torch.int32, device="cuda"),
+         "row_start": dev["row_start"], "row_end": dev["row_end"]}
+    got = run_decode(t, inp.K)
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_bad_sequences_and_pages_fail_closed():
+    _need_gpu()
+    d = synth.make_decode_inputs(6, 1, 700, 3000, 512, seed=9)
+    d.seq_of_row[0] = 6                                   # no such sequence
+    d.seq_of_row[1] = -1
+    d.block_table[2, 3] = d.k_pages.shape[0] + 5          # page 3 of sequence 2 outside the cache
+    d.row_start[3], d.row_end[3] = 5, 2                   # end < start
+    t = _dev(d)
+    mqa.mqa_fp4_status()
+    raw, slot, cnt, score = run_decode(t, 512)
+    assert mqa.mqa_fp4_status() == mqa.STATUS_BAD_WINDOW | mqa.STATUS_BAD_PAGE
+    for r, code in ((0, -1), (1, -1), (2, -2), (3, -1)):
+        assert cnt[r] == code and np.all(raw[r] == -1) and np.all(slot[r] == -1), r
+    check_decode(d, (raw, slot, cnt, score), rows=[4, 5], where="neighbours")
+
+
+def test_workspace_too_small_is_rejected():
+    _need_gpu()
+    import torch
+    d = synth.make_decode_inputs(2, 1, 600, 900, 512, seed=3)
+    t = _dev(d)
+    outs = mqa.alloc_outputs(d.Q, 512, "cuda")
+    need = mqa.mqa_fp4_decode_workspace_bytes(d.Q, 512, 4)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mqa.MQAError) as e:
+        mqa.mqa_fp4_topk_decode(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], t["block_table"],
+                                t["seq_of_row"], t["row_start"], t["row_end"], 512, *outs[:3], ws, splits=4)
+    assert e.value.code == -4
+
+
+def test_graph_capture_and_replays_match_eager():
+    """Captured once, replayed several times with different inputs copied into
+    the captured buffers eagerly between replays; every replay equals the eager
+    result for the inputs it saw."""
+    _need_gpu()
+    import torch
+    K = 1024
+    da = synth.make_decode_inputs(8, 2, 800, 6000, K, seed=21)
+    db = synth.make_decode_inputs(8, 2, 800, 6000, K, seed=22)
+    # same shapes for both sets: share the block table / windows of `a`, new data for `b`
+    db.block_table, db.seq_of_row, db.row_start, db.row_end = da.block_table, da.seq_of_row, da.row_start, da.row_end
+    db.k_pages, db.k_scale = db.k_pages[:da.k_pages.shape[0]], db.k_scale[:da.k_scale.shape[0]]
+    ta, tb = _dev(da), _dev(db)
+    assert all(ta[n].shape == tb[n].shape for n in ta)
+    want_a, want_b = run_decode(ta, K), run_decode(tb, K)
+    static = {n: v.clone() for n, v in ta.items()}
+    Q = da.Q
+    outs = mqa.alloc_outputs(Q, K, "cuda", with_score=True)
+    ws = torch.empty(mqa.mqa_fp4_decode_workspace_bytes(Q, K), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):        # warm the library outside capture (device info, module load)
+        mqa.mqa_fp4_topk_decode(static["q"], static["q_scale"], static["k_pages"], static["k_scale"],
+                                static["weights"], static["block_table"], static["seq_of_row"], static["row_start"],
+                                static["row_end"], K, outs[0], outs[1], outs[2], ws, out_score=outs[3], stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mqa.mqa_fp4_topk_decode(static["q"], static["q_scale"], static["k_pages"], static["k_scale"],
+                                static["weights"], static["block_table"], static["seq_of_row"], static["row_start"],
+                                static["row_end"], K, outs[0], outs[1], outs[2], ws, out_score=outs[3])
+    for rep, (src, want) in enumerate([(tb, want_b), (ta, want_a), (tb, want_b), (ta, want_a)]):
+        for n in static:
+            static[n].copy_(src[n])
+        for o in outs:
+            o.fill_(-9)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.cpu().numpy() for o in outs]
+        for a, b in zip(want, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), rep
+    assert mqa.mqa_fp4_status() == 0
+
+
+def test_decode_shape_long_contexts_sampled_rows():
+    """64 sequences x 1 row, C4 contexts 30,000..131,072, K = 1024; 6 rows checked."""
+    _need_gpu()
+    d = synth.make_decode_inputs(64, 1, 30000, 131072, 1024, seed=64)
+    res = run_decode(_dev(d), 1024)
+    check_decode(d, res, rows=[0, 17, 31, 40, 55, 63], where="decode long")
+    n = d.lengths()
+    assert np.all(res[2] == np.minimum(n, 1024))
