@@ -71,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_tiled_scratch_bytes.argtypes = [i64, i32, i32]
         L.mqa_fp4_tiled_scratch_bytes.restype = i64
         L.mqa_fp4_topk_decode.argtypes = [P, P, i64, P, P, i64, P, P, i64, i64, P, P, P, i32, P, P, P, P, P, i64,
-                                          i32, P]
+                                          i32, u32, P]
         L.mqa_fp4_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
         L.mqa_fp4_decode_workspace_bytes.restype = i64
         L.mqa_fp4_cache_write.argtypes = [P, i64, P, P, i64, i64, P, P, P]
@@ -227,7 +227,7 @@ def mqa_fp4_decode_workspace_bytes(num_rows: int, K: int, splits: int = 0, devic
 
 
 def mqa_fp4_topk_decode(q, q_scale, k_pages, k_scale, weights, block_table, seq_of_row, row_start, row_end, K,
-                        out_raw, out_slot, out_count, workspace, out_score=None, splits=0, stream=None):
+                        out_raw, out_slot, out_count, workspace, out_score=None, splits=0, flags=0, stream=None):
     """Decode / multi-sequence form: block_table int32 [n_seq, max_pages], seq_of_row int32 [Q],
     workspace a uint8 device tensor of at least mqa_fp4_decode_workspace_bytes(Q, K, splits) bytes.
     Allocates nothing and does not synchronise (capturable)."""
@@ -247,7 +247,7 @@ def mqa_fp4_topk_decode(q, q_scale, k_pages, k_scale, weights, block_table, seq_
         _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), k_pages.shape[0], _ptr(weights),
         _ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(seq_of_row), _ptr(row_start),
         _ptr(row_end), int(K), _ptr(out_raw), _ptr(out_slot), _ptr(out_count), _ptr(out_score), _ptr(workspace),
-        workspace.numel(), int(splits), _stream(stream, q.device))
+        workspace.numel(), int(splits), int(flags), _stream(stream, q.device))
     _rc(rc, "mqa_fp4_topk_decode")
 
 

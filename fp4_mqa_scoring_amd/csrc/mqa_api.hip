@@ -519,8 +519,12 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
                             const int32_t* block_table, int64_t num_seqs, int64_t max_pages,
                             const int32_t* seq_of_row, const int32_t* row_start, const int32_t* row_end, int32_t K,
                             int32_t* out_raw, int32_t* out_slot, int32_t* out_count, float* out_score,
-                            void* workspace, int64_t workspace_bytes, int32_t splits, void* stream) {
+                            void* workspace, int64_t workspace_bytes, int32_t splits, uint32_t flags,
+                            void* stream) {
   if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
+  if (flags & ~(MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
+  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
+  const int mode = (flags & MQA_FLAG_NO_PREFILTER) ? 1 : (flags & MQA_FLAG_FORCE_UNDERFILL) ? 2 : 0;
   int32_t rc = check_sizes(num_rows, num_phys_pages, max_pages);
   if (rc != MQA_OK) return rc;
   if (num_seqs < 0 || (max_pages > 0 && num_seqs > 0x7FFFFFFFll / max_pages)) return MQA_ERR_BAD_SIZE;
@@ -545,8 +549,8 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
   p.seq_of_row = seq_of_row;
   p.n_seq = num_seqs;
   const mqa::DecodeScratch w = mqa::decode_scratch_layout(workspace, num_rows, K, sp);
-  rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, nullptr, st));
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, st));
+  rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, w.fb_count, st));
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, mode, st));
   return rc;
 }
 

@@ -58,13 +58,22 @@ hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32
 // own pages, then an exact merge of the splits. Scratch comes from the caller.
 struct DecodeScratch {
   int32_t* row_state;   // [Q]
-  int32_t* counts;      // [Q, splits]
-  uint64_t* keys;       // [Q, splits, K]
+  int32_t* counts;      // [Q, splits]      fallback: keys per (row, split)
+  uint64_t* keys;       // [Q, splits, K]   fallback: top-K per (row, split)
+  uint64_t* samples;    // [Q, splits, kDecSampleCap] calibration keys
+  int32_t* sample_n;    // [Q, splits]
+  uint64_t* gate;       // [Q]
+  uint32_t* cand_n;     // [Q]              candidates appended (may exceed cap: overflow)
+  uint64_t* cand;       // [Q, candidate_cap(K)]
+  int32_t* fb_list;     // [Q]              rows sent to the fallback
+  int32_t* fb_count;    // [1]              (cleared by row_prep)
 };
 constexpr int kMaxDecodeSplits = 64;
+constexpr int kDecSampleCap = 128;   // calibration keys kept per (row, split); k' <= 104
 size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
-hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, hipStream_t st);
+// mode 0 gated, 1 no prefilter (every long row takes the exact fallback), 2 forced underfill.
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st);
 
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.

@@ -206,4 +206,11 @@ __device__ __forceinline__ void fail_row(int64_t row, int code, int32_t* __restr
 }
 
 
+// Candidates the sample must keep: x + 4 sqrt(x) + 8 where x = K m / n is the
+// expected number of the row's true top-K positions among m sampled ones.
+__device__ __forceinline__ int sample_keep(int K, int m, int n) {
+  const float x = static_cast<float>(K) * static_cast<float>(m) / static_cast<float>(n);
+  return static_cast<int>(ceilf(x + 4.0f * sqrtf(x) + 8.0f));
+}
+
 }  // namespace mqa

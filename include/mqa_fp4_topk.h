@@ -222,17 +222,23 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
  * The call allocates nothing, never synchronises and accepts a capturing
  * stream; row failures are reported in out_count and the sticky status word
  * only (read mqa_fp4_status outside the graph). Each row is scanned
- * independently (no key sharing between rows): one wave per (row, split)
- * streams the row's pages through a bounded LDS pool with exact radix
- * compaction, then the splits are merged exactly. Two calls that share a
- * workspace must be ordered (same stream).
+ * independently (no key sharing between rows), one wave per (row, split): a
+ * calibrated gate from every 16th page (PR 5309's calibrated candidate filter),
+ * a gated scan into a bounded per-row candidate buffer and an exact merge; rows
+ * that underfill or overflow are recomputed exactly by per-wave bounded LDS
+ * pools (PR 5282's streaming design) with an exact merge of the splits. flags:
+ * MQA_FLAG_NO_PREFILTER or MQA_FLAG_FORCE_UNDERFILL (for tests; the split bits
+ * must be 0, splits are the separate argument). Outputs do not depend on the
+ * splits or the flags. Two calls that share a workspace must be ordered (same
+ * stream).
  */
 int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows, const uint8_t* k_pages,
                             const uint8_t* k_scale, int64_t num_phys_pages, const float* weights,
                             const int32_t* block_table, int64_t num_seqs, int64_t max_pages,
                             const int32_t* seq_of_row, const int32_t* row_start, const int32_t* row_end, int32_t K,
                             int32_t* out_raw, int32_t* out_slot, int32_t* out_count, float* out_score,
-                            void* workspace, int64_t workspace_bytes, int32_t splits, void* stream);
+                            void* workspace, int64_t workspace_bytes, int32_t splits, uint32_t flags,
+                            void* stream);
 int64_t mqa_fp4_decode_workspace_bytes(int64_t num_rows, int32_t K, int32_t splits, int32_t device);
 
 /*

@@ -134,10 +134,12 @@ def test_decode_entry_checks_arguments_on_host(lib):
     P = ctypes.c_void_p
     p = P(0x1000)
 
-    def call(K=512, splits=0, ws=p, ws_bytes=1 << 20):
+    def call(K=512, splits=0, ws=p, ws_bytes=1 << 20, flags=0):
         return lib.mqa_fp4_topk_decode(p, p, 2, p, p, 4, p, p, 2, 4, p, p, p, K, p, p, p, None, ws, ws_bytes,
-                                       splits, None)
+                                       splits, flags, None)
     assert call(K=100) == -1
+    assert call(flags=0x3) == -8                     # split bits belong to the splits argument
+    assert call(flags=0x300) == -8                   # no prefilter + forced underfill
     assert call(splits=65) == -4
     assert call(splits=-1) == -4
     assert call(ws_bytes=-1) == -4
@@ -146,4 +148,7 @@ def test_decode_entry_checks_arguments_on_host(lib):
     # explicit splits: no device query; O(Q) + Q*splits*(4 + 8K) bytes
     q, K, s = 100, 1024, 5
     a = lambda x: (x + 255) // 256 * 256
-    assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == a(q * 4) + a(q * s * 4) + a(q * s * K * 8)
+    cap = 2560                                       # candidate keys per row at K = 1024
+    want = (a(q * 4) + a(q * s * 4) + a(q * s * K * 8) + a(q * s * 128 * 8) + a(q * s * 4) + a(q * 8) + a(q * 4)
+            + a(q * cap * 8) + a(q * 4) + a(4))
+    assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == want

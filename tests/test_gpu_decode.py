@@ -27,7 +27,7 @@ def _dev(d):
                       "row_end")}
 
 
-def run_decode(t, K, splits=0, with_score=True):
+def run_decode(t, K, splits=0, with_score=True, flags=0):
     import torch
     Q = t["q"].shape[0]
     outs = mqa.alloc_outputs(Q, K, t["q"].device, with_score=with_score)
@@ -36,7 +36,7 @@ def run_decode(t, K, splits=0, with_score=True):
     ws = torch.empty(mqa.mqa_fp4_decode_workspace_bytes(Q, K, splits), dtype=torch.uint8, device="cuda")
     mqa.mqa_fp4_topk_decode(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], t["block_table"],
                             t["seq_of_row"], t["row_start"], t["row_end"], K, outs[0], outs[1], outs[2], ws,
-                            out_score=outs[3] if with_score else None, splits=splits)
+                            out_score=outs[3] if with_score else None, splits=splits, flags=flags)
     torch.cuda.synchronize()
     return [o.cpu().numpy() for o in outs]
 
@@ -66,6 +66,25 @@ def test_splits_do_not_change_outputs():
         got = run_decode(t, 1024, splits=s)
         for a, b in zip(base, got):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), s
+
+
+@pytest.mark.parametrize("K", [512, 1024])
+def test_gate_off_and_forced_underfill_give_identical_outputs(K):
+    """The calibrated gate, no gate (every row through the exact pool fallback)
+    and a forced underfill (gate above every key, then the fallback) agree bit for
+    bit; tie rows (all-equal scores) included."""
+    _need_gpu()
+    d = synth.make_decode_inputs(9, 2, K + 1, 20000, K, seed=91 + K)
+    d.q[3] = 0
+    d.q[8] = 0
+    t = _dev(d)
+    base = run_decode(t, K)
+    check_decode(d, base, where=f"gated K={K}")
+    for flags in (mqa.FLAG_NO_PREFILTER, mqa.FLAG_FORCE_UNDERFILL):
+        got = run_decode(t, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+    assert mqa.mqa_fp4_status() == 0
 
 
 def test_one_sequence_equals_the_prefill_path():
