@@ -262,15 +262,19 @@ def bench_decode(args, torch, mqa, dev):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     graph_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    # eager calls, and the scan kernel alone from the library's own stage boundaries:
-    # timed as the eager call minus row preparation and merge, measured separately below
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
+    # eager calls with the library's stage events: the gated scan kernel alone
+    hev = HipEvents()
+    sev = [hev.create(5) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / args.steps
+    for e in sev:
+        mqa.mqa_fp4_set_stage_events(e)
+        call()
+    mqa.mqa_fp4_set_stage_events(None)
+    torch.cuda.synchronize()
+    eager_ms = float(np.mean([hev.elapsed_ms(e[0], e[4]) for e in sev]))
+    scan_ms = float(np.mean([hev.elapsed_ms(e[2], e[3]) for e in sev]))
+    for e in sev:
+        hev.destroy(e)
     assert mqa.mqa_fp4_status(stream) == 0
     counts = outs[2].cpu().numpy()
     n = d.lengths()
@@ -283,11 +287,12 @@ def bench_decode(args, torch, mqa, dev):
         "vs_baseline": None, "dtype": "mxfp4 x mxfp4 -> f32", "data": "synthetic",
         "config": {"workload": "decode: 64 sequences x 1 row, C4 context 32768..131072, K=1024",
                    "Q": Q, "K": K, "scored_pairs": pairs, "workspace_bytes": ws.numel()},
-        "roofline": {"bound": "hbm", "achieved": key_bytes / (graph_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": key_bytes / (graph_ms * 1e-3) / HBM_PEAK, "traffic": None,
-                     "kernel": "decode call (row prep + decode_scan_kernel<1024> + decode_merge_kernel<1024>)",
-                     "graph_replay_ms": graph_ms, "eager_ms": eager_ms,
-                     "mfma_frac": pairs * FLOP_PER_PAIR / (graph_ms * 1e-3) / MXFP4_PEAK},
+        "roofline": {"bound": "hbm", "achieved": key_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": key_bytes / (scan_ms * 1e-3) / HBM_PEAK, "traffic": None,
+                     "kernel": "decode_gscan_kernel<1024>", "kernel_ms": scan_ms,
+                     "graph_replay_ms": graph_ms, "eager_call_ms": eager_ms,
+                     "call_key_gbs": key_bytes / (graph_ms * 1e-3) / 1e9,
+                     "mfma_frac": pairs * FLOP_PER_PAIR / (scan_ms * 1e-3) / MXFP4_PEAK},
         "checks_ok": ok,
         "cpu_baseline": None,
     }

@@ -549,8 +549,11 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
   p.seq_of_row = seq_of_row;
   p.n_seq = num_seqs;
   const mqa::DecodeScratch w = mqa::decode_scratch_layout(workspace, num_rows, K, sp);
+  record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, w.fb_count, st));
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, mode, st));
+  record_stage(1, st);
+  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, mode, st, t_stage_events ? record_stage : nullptr));
+  record_stage(4, st);
   return rc;
 }
 

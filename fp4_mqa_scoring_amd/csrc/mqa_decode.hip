@@ -524,7 +524,8 @@ __global__ void __launch_bounds__(1024) decode_fb_merge_kernel(DecArgs a, int32_
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 template <int K>
-void launch_decode_k(const DecArgs& a, const PathArgs& p, int mode, int32_t* status, hipStream_t st) {
+void launch_decode_k(const DecArgs& a, const PathArgs& p, int mode, int32_t* status, hipStream_t st,
+                     StageMark mark) {
   const int64_t items = p.Q * a.splits;
   const dim3 sgrid(static_cast<unsigned>((items + kDecWaves - 1) / kDecWaves));
   const dim3 rgrid(static_cast<unsigned>(p.Q));
@@ -532,7 +533,9 @@ void launch_decode_k(const DecArgs& a, const PathArgs& p, int mode, int32_t* sta
   const dim3 fgrid(static_cast<unsigned>(fb_cap < kDecFallbackBlocks ? fb_cap : kDecFallbackBlocks));
   decode_calib_kernel<K><<<sgrid, dim3(kDecThreads), 0, st>>>(a);
   decode_gate_kernel<K><<<rgrid, dim3(1024), 0, st>>>(a, mode);
+  if (mark) mark(2, st);   // before the gated scan
   decode_gscan_kernel<K><<<sgrid, dim3(kDecThreads), 0, st>>>(a);
+  if (mark) mark(3, st);   // after it
   decode_gmerge_kernel<K><<<rgrid, dim3(1024), 0, st>>>(a, p.out_raw, p.out_slot, p.out_count, p.out_score, status);
   decode_fb_scan_kernel<K><<<fgrid, dim3(kDecThreads), 0, st>>>(a);
   const unsigned mblocks = static_cast<unsigned>(p.Q < kDecFallbackBlocks ? p.Q : kDecFallbackBlocks);
@@ -575,7 +578,8 @@ DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t sp
   return w;
 }
 
-hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st) {
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st,
+                         StageMark mark) {
   if (p.Q == 0) return hipSuccess;
   int32_t* status = status_word();
   if (status == nullptr) return hipErrorInvalidSymbol;
@@ -596,8 +600,8 @@ hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t spli
   a.splits = splits;
   a.w = w;
   a.cap = candidate_cap(p.K);
-  if (p.K == 512) launch_decode_k<512>(a, p, mode, status, st);
-  else launch_decode_k<1024>(a, p, mode, status, st);
+  if (p.K == 512) launch_decode_k<512>(a, p, mode, status, st, mark);
+  else launch_decode_k<1024>(a, p, mode, status, st, mark);
   return hipGetLastError();
 }
 

@@ -72,8 +72,11 @@ constexpr int kMaxDecodeSplits = 64;
 constexpr int kDecSampleCap = 128;   // calibration keys kept per (row, split); k' <= 104
 size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
+// Measurement marker called between launches (index, stream); may be null.
+typedef void (*StageMark)(int, hipStream_t);
 // mode 0 gated, 1 no prefilter (every long row takes the exact fallback), 2 forced underfill.
-hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st);
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st,
+                         StageMark mark = nullptr);
 
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.

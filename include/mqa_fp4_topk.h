@@ -196,9 +196,10 @@ int32_t mqa_fp4_status(void* stream, int32_t* status);
 /* Measurement hook. After this call, every fused or dense TopK call made by
  * the calling host thread records the n == 5 caller-created hipEvent_t handles
  * in events[] on the call's stream: [0] before row preparation, [1] before the
- * gate calibration, [2] before the scoring kernel (fused: the gated scan; dense:
- * the logits kernel; [1] and [2] coincide on the dense path), [3] after it, [4]
- * after the last kernel of the call. The array must stay valid until the hook
+ * gate calibration, [2] before the scoring kernel (fused and decode: the gated
+ * scan; dense: the logits kernel; [1] and [2] coincide on the dense path), [3]
+ * after it, [4] after the last kernel of the call. (The tiled path records them
+ * too, around all of its tiles.) The array must stay valid until the hook
  * is replaced; n == 0 (or events == NULL) turns it off. Adds no
  * synchronisation. Returns MQA_ERR_BAD_SIZE for other n. */
 int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
