@@ -1,11 +1,11 @@
 // Decode / multi-sequence variant of the FP4 paged-MQA indexer with exact TopK
 // (gfx950). Every row has its own page table (block table row seq_of_row[r]),
 // so rows share no key tiles: each wave streams one (row, context split) item's
-// pages by itself, the way the pages' first fused design keeps a bounded pool
-// per CTA ("[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK", Changes: scores
-// stream through a bounded LDS pool, exact total-order radix, each CTA emits
-// only candidates and a count, splits merged exactly, raw positions mapped
-// through the page table). Decode workloads are the adjacent shape the pages
+// pages by itself, the way the pages' first fused design works per CTA
+// ("[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK", Changes: running
+// candidates held in a fixed-size LDS pool, an exact radix selection on the
+// total-order key, only candidates and their number handed on, an exact merge
+// of the splits, then the page-table mapping). Decode workloads are the adjacent shape the pages
 // leave on the older path ("[AMD][DSv4] Add experimental AITER FP4 streaming
 // TopK", Changes / Scope) and whose graph-capture support they defer ([P2]
 // Scope); this entry point takes its scratch from the caller, never allocates
