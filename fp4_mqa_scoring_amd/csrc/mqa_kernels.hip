@@ -128,7 +128,27 @@ struct CandArgs {
   int32_t cap;
 };
 
-constexpr int kCalStride = 16;       // the calibration samples every 16th position
+template <int K>
+struct Geometry;
+template <>
+struct Geometry<512> {
+  static constexpr int kCap = 2048;
+  static constexpr int kFbSplits = 4;
+};
+template <>
+struct Geometry<1024> {
+  static constexpr int kCap = 2560;
+  static constexpr int kFbSplits = 2;
+};
+// Fallback pool per row: all LDS left after the block buffers and histograms.
+constexpr int kPoolCap = 1856;
+constexpr int kFallbackGrid = 256;
+
+// The calibration samples every 16th position. (A stride of 32 halves its cost
+// but the coarser gate sends rows to the exact fallback: measured slower.)
+constexpr int kCalStride = 16;
+constexpr int kCalPerPage = kPage / kCalStride;   // sampled positions per page
+static_assert(kCalStride >= 16 && kCalStride <= kPage && kPage % kCalStride == 0, "stride divides the page");
 constexpr int kCalCap = 512;         // calibration pool per row
 constexpr int kStageCap = 256;       // per-wave LDS staging of candidate keys
 
@@ -236,7 +256,7 @@ struct SampleDma {
   // addresses it would otherwise keep for the whole scan do not fit the
   // 128-VGPR budget of four waves per SIMD.
   struct Lane {
-    int pg0, pg1, pg_sc;      // page index inside a sample block (0..63)
+    int pg0, pg1, pg_sc;      // page index inside a sample block
     int off0, off1, off_sc;   // byte offset inside the source page
   };
   __device__ __forceinline__ Lane lane_layout() const {
@@ -244,9 +264,10 @@ struct SampleDma {
     __asm__ __volatile__("v_and_b32 %0, 63, %1" : "=v"(lane) : "v"(static_cast<int>(threadIdx.x)));
     const int pq = lane >> 2, slot = lane & 3;
     const int p0 = run + pq, p1 = p0 + 16, ps = run + (lane & 31);
-    return Lane{p0 >> 2, p1 >> 2, ps >> 2, kCalStride * (p0 & 3) * kVecBytes + 16 * (slot ^ chunk_swizzle(p0)),
-                kCalStride * (p1 & 3) * kVecBytes + 16 * (slot ^ chunk_swizzle(p1)),
-                kCalStride * (ps & 3) * kVecScales};
+    return Lane{p0 / kCalPerPage, p1 / kCalPerPage, ps / kCalPerPage,
+                kCalStride * (p0 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p0)),
+                kCalStride * (p1 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p1)),
+                kCalStride * (ps % kCalPerPage) * kVecScales};
   }
 
   struct Ent {
@@ -260,7 +281,7 @@ struct SampleDma {
   }
   __device__ __forceinline__ Ent entries(const ScanArgs& a, int v, int) const {
     const Lane l = lane_layout();
-    const int b = base_pg + v * (kTile / 4);   // sample block v spans 64 pages
+    const int b = base_pg + v * (kTile / kCalPerPage);   // sample block v spans kTile / kCalPerPage pages
     return Ent{entry(a, b + l.pg0), entry(a, b + l.pg1), entry(a, b + l.pg_sc)};
   }
 
@@ -924,21 +945,6 @@ __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restric
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
 }
 
-template <int K>
-struct Geometry;
-template <>
-struct Geometry<512> {
-  static constexpr int kCap = 2048;
-  static constexpr int kFbSplits = 4;
-};
-template <>
-struct Geometry<1024> {
-  static constexpr int kCap = 2560;
-  static constexpr int kFbSplits = 2;
-};
-// Fallback pool per row: all LDS left after the block buffers and histograms.
-constexpr int kPoolCap = 1856;
-constexpr int kFallbackGrid = 256;
 static_assert(Geometry<512>::kFbSplits * 512 <= Geometry<512>::kCap, "fallback keys fit the candidate buffer");
 static_assert(Geometry<1024>::kFbSplits * 1024 <= Geometry<1024>::kCap, "fallback keys fit the candidate buffer");
 
