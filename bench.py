@@ -57,7 +57,7 @@ def code_hash(*files: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    return code_hash("mqa_device.h", "mqa_kernels.hip")
+    return code_hash("mqa_device.h", "mqa_select.h", "mqa_kernels.hip")
 
 
 class HipEvents:

@@ -863,6 +863,8 @@ __global__ void __launch_bounds__(1024) logits_topk_kernel(
 // is the window's top-K. No gate, no calibration; scratch Q * (4 tile + 8 K)
 // bytes, independent of the context length.
 // ---------------------------------------------------------------------------
+constexpr int kTileNewCap = 1024;   // tile keys above the running minimum held in LDS
+
 __global__ void __launch_bounds__(256) tile_reset_kernel(int32_t* __restrict__ run_count, int64_t Q) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < Q) run_count[i] = 0;
@@ -877,9 +879,11 @@ __global__ void __launch_bounds__(256) tile_merge_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ run_count) {
   constexpr int NT = 256;
   __shared__ uint64_t s_run[K];
+  __shared__ uint64_t s_new[kTileNewCap];
   __shared__ uint32_t s_hist[256];
   __shared__ BlockScratch<NT> s_red;
-  __shared__ int32_t s_n;
+  __shared__ int32_t s_n, s_m;
+  __shared__ uint64_t s_min;
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
   const int32_t a = max(row_start[row], lo), b = min(row_end[row], hi);
@@ -896,6 +900,54 @@ __global__ void __launch_bounds__(256) tile_merge_kernel(const int32_t* __restri
     return true;
   };
   const int64_t n = static_cast<int64_t>(n_run) + n_tile;
+  if (n_run == K) {
+    // The running set is full: only tile keys above its smallest key can enter.
+    // One pass over the tile collects those into LDS; the select then runs over
+    // LDS only (unless too many enter, then the general path below).
+    if (threadIdx.x == 0) {
+      s_min = ~0ull;
+      s_m = 0;
+    }
+    __syncthreads();
+    uint64_t mn = ~0ull;
+    for (int i = threadIdx.x; i < K; i += NT) mn = min(mn, s_run[i]);
+    atomicMin(&s_min, mn);
+    __syncthreads();
+    const uint64_t floor_key = s_min;
+    for (int i = threadIdx.x; i < n_tile; i += NT) {
+      const uint64_t x = make_key(lg[i], static_cast<uint32_t>(a + i));
+      if (x > floor_key) {
+        const int at = atomicAdd(&s_m, 1);
+        if (at < kTileNewCap) s_new[at] = x;
+      }
+    }
+    __syncthreads();
+    const int m = s_m;
+    if (m == 0) return;   // nothing of this tile reaches the row's top K
+    if (m <= kTileNewCap) {
+      auto lsrc = [&](int64_t i, uint64_t& x) -> bool {
+        x = i < K ? s_run[i] : s_new[i - K];
+        return true;
+      };
+      bool ok = false;
+      const uint64_t T = block_radix_select<NT, 8>(lsrc, K + m, K, s_hist, s_red, &ok);
+      if (threadIdx.x == 0) s_n = 0;
+      __syncthreads();
+      if (ok) {
+        for (int i = threadIdx.x; i < K + m; i += NT) {
+          uint64_t x;
+          lsrc(i, x);
+          if (x >= T) {
+            const int at = atomicAdd(&s_n, 1);
+            if (at < K) run[at] = x;
+          }
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) run_count[row] = (ok && s_n == K) ? K : -1;
+      return;
+    }
+  }
   if (n <= K) {   // everything fits: append the tile's keys
     for (int i = threadIdx.x; i < n_tile; i += NT) {
       uint64_t x;
