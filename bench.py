@@ -397,11 +397,12 @@ def main():
     kern_valu = pairs * VALU_PER_PAIR / (kern * 1e-3)
 
     # sustained peaks of this device under the same conditions (outside the timed region)
-    peaks = {}
+    peaks, probe_ms = {}, {}
     p_blocks, p_iters = 2048, 2000
     pout = torch.empty(p_blocks * 512, dtype=torch.float32, device=dev)
     for kind, name, work in ((0, "mxfp4_mfma_tflops", p_blocks * 8 * p_iters * 4 * FLOP_PER_MFMA),
-                             (1, "fp32_fma_tops", p_blocks * 512 * p_iters * 64)):
+                             (1, "fp32_fma_tops", p_blocks * 512 * p_iters * 64),
+                             (2, None, 0)):
         for _ in range(2):
             mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -410,8 +411,14 @@ def main():
             mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        peaks[name] = work / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12
+        probe_ms[kind] = e0.elapsed_time(e1) / 5
+        if name:
+            peaks[name] = work / (probe_ms[kind] * 1e-3) / 1e12
     del pout
+    # one MFMA wave and one FMA wave per SIMD: 0 = the SIMD runs the two one after
+    # the other (time = half of each pure run), 1 = fully overlapped (time = the larger half)
+    half_m, half_f = probe_ms[0] / 2, probe_ms[1] / 2
+    overlap = (half_m + half_f - probe_ms[2]) / min(half_m, half_f)
 
     # alternating dense / fused pairs, outside the timed region
     dense = None
@@ -508,7 +515,10 @@ def main():
                      "measured_fp32_fma_tops": peaks["fp32_fma_tops"],
                      "mfma_plus_valu_frac_measured": pairs * (FLOP_PER_PAIR / (peaks["mxfp4_mfma_tflops"] * 1e12)
                                                               + VALU_PER_PAIR / (peaks["fp32_fma_tops"] * 1e12))
-                                                     / (kern * 1e-3)},
+                                                     / (kern * 1e-3),
+                     "simd_mfma_valu_overlap": overlap,
+                     "overlap_probe_ms": {"mfma_only": probe_ms[0], "fma_only": probe_ms[1],
+                                          "one_of_each_per_simd": probe_ms[2]}},
         "mxfp4_tflops_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / 1e12,
         "mxfp4_peak_frac_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / MXFP4_PEAK,
         "stage_ms": {"row_prep": float(np.mean(prep_ms)), "calibration": float(np.mean(calib_ms)),

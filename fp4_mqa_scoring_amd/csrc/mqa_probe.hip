@@ -1,7 +1,9 @@
-// Peak probes: a pure MXFP4 MFMA loop and a pure fp32 FMA loop, launched on the
-// caller's stream so that the sustained rates can be measured under the same
-// clocks and power state the operator runs in (MI355X's published peaks are
-// quoted at 2.4 GHz; the shader clock is lower under dense MFMA load).
+// Peak probes: a pure MXFP4 MFMA loop, a pure fp32 FMA loop and the two side by
+// side on every SIMD, launched on the caller's stream so that the sustained
+// rates, and whether a SIMD overlaps the two kinds of work, can be measured
+// under the same clocks and power state the operator runs in (MI355X's
+// published peaks are quoted at 2.4 GHz; the shader clock is lower under dense
+// MFMA load).
 #include "mqa_device.h"
 #include "mqa_fp4_topk.h"
 
@@ -12,8 +14,7 @@ constexpr int kProbeThreads = 512;
 
 // Four independent accumulator chains per wave, one 32x32x64 FP4 MFMA each per
 // iteration (2*32*32*64 FLOP). Codes and scales are arbitrary finite values.
-__global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(int iters, float* __restrict__ out) {
-  const int l = threadIdx.x & 63;
+__device__ __noinline__ float mfma_loop(int iters, int l) {
   const v4i a = {l * 0x01010101, l * 0x03030303, l * 0x05050505, l * 0x07070707};
   v4i b = a ^ v4i{0x55555555, 0x33333333, 0x0F0F0F0F, 0x11111111};
   const int sc = 0x7F7F7F7F;
@@ -24,12 +25,11 @@ __global__ void __launch_bounds__(kProbeThreads) mfma_probe_kernel(int iters, fl
     c2 = mfma_fp4<0, 0>(a, b, c2, sc, sc);
     c3 = mfma_fp4<0, 0>(a, b, c3, sc, sc);
   }
-  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = c0[0] + c1[1] + c2[2] + c3[3];
+  return c0[0] + c1[1] + c2[2] + c3[3];
 }
 
 // Eight independent chains, 64 fp32 FMAs per lane per iteration.
-__global__ void __launch_bounds__(kProbeThreads) fma_probe_kernel(int iters, float* __restrict__ out) {
-  const int l = threadIdx.x & 63;
+__device__ __noinline__ float fma_loop(int iters, int l) {
   float w[16], x[16], p[8];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -48,20 +48,29 @@ __global__ void __launch_bounds__(kProbeThreads) fma_probe_kernel(int iters, flo
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) s += p[c];
-  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = s;
+  return s;
+}
+
+// kind 0: every wave runs the MFMA loop; 1: every wave the FMA loop; 2: waves
+// 0-3 of the block the MFMA loop and waves 4-7 the FMA loop. Wave w of a block
+// runs on SIMD w % 4, so with kind 2 each SIMD holds one wave of each: its time
+// against half of kind 0's plus half of kind 1's shows whether the SIMD runs
+// MFMA and VALU work at the same time.
+__global__ void __launch_bounds__(kProbeThreads) peak_probe_kernel(int kind, int iters, float* __restrict__ out) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const bool mfma = kind == 0 || (kind == 2 && w < 4);
+  const float v = mfma ? mfma_loop(iters, l) : fma_loop(iters, l);
+  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = v;
 }
 
 }  // namespace
 }  // namespace mqa
 
 extern "C" int32_t mqa_fp4_peak_probe(int32_t kind, float* out, int32_t blocks, int32_t iters, void* stream) {
-  if ((kind != 0 && kind != 1) || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
+  if (kind < 0 || kind > 2 || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
   if (out == nullptr) return MQA_ERR_NULL_POINTER;
   if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return MQA_ERR_MISALIGNED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (kind == 0)
-    mqa::mfma_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(iters, out);
-  else
-    mqa::fma_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(iters, out);
+  mqa::peak_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
   return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }

@@ -279,7 +279,12 @@ int32_t mqa_fp4_cache_write(const float* k, int64_t n, const int32_t* positions,
 /* Measurement hook: sustained-peak probes on `stream` (no operator work).
  * kind 0: a pure MXFP4 MFMA loop, blocks x 8 waves x iters x 4
  *         v_mfma_scale_f32_32x32x64_f8f6f4 (2*32*32*64 FLOP each);
- * kind 1: a pure fp32 FMA loop, blocks x 512 lanes x iters x 64 FMAs.
+ * kind 1: a pure fp32 FMA loop, blocks x 512 lanes x iters x 64 FMAs;
+ * kind 2: in every 512-thread block waves 0-3 run the kind-0 loop and waves
+ *         4-7 the kind-1 loop, i.e. one wave of each per SIMD (both halves of
+ *         the work of kinds 0 and 1): a time near half of kind 0's plus half of
+ *         kind 1's means the SIMD runs MFMA and VALU work one after the other,
+ *         near the larger half means it overlaps them.
  * out: device float[blocks * 512], written once per lane (keeps the work live).
  * MI355X's published peaks are quoted at 2.4 GHz; timing these launches gives
  * the rates under the clocks the operator actually sees. Returns
