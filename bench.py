@@ -402,7 +402,7 @@ def main():
     pout = torch.empty(p_blocks * 512, dtype=torch.float32, device=dev)
     for kind, name, work in ((0, "mxfp4_mfma_tflops", p_blocks * 8 * p_iters * 4 * FLOP_PER_MFMA),
                              (1, "fp32_fma_tops", p_blocks * 512 * p_iters * 64),
-                             (2, None, 0)):
+                             (2, None, 0), (3, None, 0), (4, None, 0), (5, None, 0)):
         for _ in range(2):
             mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -518,7 +518,11 @@ def main():
                                                      / (kern * 1e-3),
                      "simd_mfma_valu_overlap": overlap,
                      "overlap_probe_ms": {"mfma_only": probe_ms[0], "fma_only": probe_ms[1],
-                                          "one_of_each_per_simd": probe_ms[2]}},
+                                          "one_of_each_per_simd": probe_ms[2]},
+                     # LDS reads of the score-block image: the scan's pattern vs a linear
+                     # (conflict-free) one and the unswizzled image
+                     "lds_read_probe_ms": {"scan_image": probe_ms[3], "linear": probe_ms[4],
+                                           "unswizzled": probe_ms[5]}},
         "mxfp4_tflops_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / 1e12,
         "mxfp4_peak_frac_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / MXFP4_PEAK,
         "stage_ms": {"row_prep": float(np.mean(prep_ms)), "calibration": float(np.mean(calib_ms)),

@@ -166,9 +166,16 @@ __device__ __forceinline__ void load_qrow(QRow& r, const uint8_t* q_row, const u
 }
 
 // LDS image of one score block: position p's 64 code bytes at p*64, with its
-// 16-byte chunk c stored at chunk slot c ^ chunk_swizzle(p) so that the 32
-// lanes reading one chunk of 32 consecutive positions hit distinct banks.
-__device__ __forceinline__ int chunk_swizzle(int p) { return ((p >> 1) ^ (p >> 3)) & 3; }
+// 16-byte chunk c stored at chunk slot c ^ chunk_swizzle(p).
+// On gfx950 a wave's ds_read_b128 is served 16 lanes per LDS cycle across 64
+// four-byte banks, and each cycle's 16 lanes hold, for every x < 16, one of
+// lanes x and x + 16 of the wave half (bank-conflict counter on a read-pattern
+// probe: a linear pattern takes 0 extra cycles per read, the former swizzle
+// ((p >> 1) ^ (p >> 3)) & 3 took 4, no swizzle 12). The lane reading chunk c of
+// position r (r < 32) hits bank quad 4 (r & 3) + (c ^ chunk_swizzle(r)) mod 16;
+// the four lanes of a cycle that share r & 3 differ in bits 2..3 of r, so with
+// the swizzle taken from those bits all 16 quads are distinct.
+__device__ __forceinline__ int chunk_swizzle(int p) { return (p >> 2) & 3; }
 
 __device__ __forceinline__ void load_keys32(const uint8_t* s_codes, const uint8_t* s_scales, int grp,
                                             int lane, v4i& b0, v4i& b1, int& ks) {

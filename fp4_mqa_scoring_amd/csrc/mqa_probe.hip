@@ -3,7 +3,8 @@
 // rates, and whether a SIMD overlaps the two kinds of work, can be measured
 // under the same clocks and power state the operator runs in (MI355X's
 // published peaks are quoted at 2.4 GHz; the shader clock is lower under dense
-// MFMA load).
+// MFMA load). Three more kinds time LDS read patterns, so that the bank
+// behaviour of the score-block image can be checked on the device.
 #include "mqa_device.h"
 #include "mqa_fp4_topk.h"
 
@@ -51,6 +52,22 @@ __device__ __noinline__ float fma_loop(int iters, int l) {
   return s;
 }
 
+// Two 16-byte LDS reads per lane per iteration from one of the eight 32-position
+// groups of a score-block image (group it % 8, 2 KB apart); inlined so that the
+// reads stay ds_read_b128 on the LDS pointer.
+constexpr int kProbeImageBytes = 8 * 32 * kVecBytes;
+__device__ __forceinline__ float lds_loop(const uint8_t* img, int o0, int o1, int iters) {
+  v4i acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    const uint8_t* g = img + (it & 7) * (32 * kVecBytes);
+    const v4i x = *reinterpret_cast<const v4i*>(g + o0);
+    const v4i y = *reinterpret_cast<const v4i*>(g + o1);
+    acc ^= x + y;
+    __asm__ __volatile__("" ::: "memory");   // no reuse of the loads across iterations
+  }
+  return static_cast<float>(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+}
+
 // kind 0: every wave runs the MFMA loop; 1: every wave the FMA loop; 2: waves
 // 0-3 of the block the MFMA loop and waves 4-7 the FMA loop. Wave w of a block
 // runs on SIMD w % 4, so with kind 2 each SIMD holds one wave of each: its time
@@ -63,14 +80,45 @@ __global__ void __launch_bounds__(kProbeThreads) peak_probe_kernel(int kind, int
   out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = v;
 }
 
+// kinds 3-5: LDS reads of a score-block image: 3 the scan's own operand reads
+// (lane_offsets, i.e. with the chunk swizzle), 4 a linear pattern (lane l reads
+// bytes 16 l .. 16 l + 15 of each 1 KB half of a group, free of bank conflicts
+// under any lane grouping), 5 the image without a swizzle. Kind 3 taking the
+// time of kind 4 means the image is read without bank conflicts.
+// Offsets stay inside a group: 3: 31*64 + 48 + 16 = 2048; 4: 1024 + 63*16 + 16
+// = 2048; 5: 31*64 + 32 + 16 + 16 = 2048.
+__global__ void __launch_bounds__(kProbeThreads) lds_probe_kernel(int kind, int iters, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_img[kProbeImageBytes];
+  const int l = threadIdx.x & 63;
+  for (int i = threadIdx.x; i < kProbeImageBytes / 4; i += kProbeThreads)
+    reinterpret_cast<uint32_t*>(s_img)[i] = static_cast<uint32_t>(i) * 2654435761u;
+  __syncthreads();
+  int o0, o1;
+  if (kind == 3) {
+    const LaneOffsets lo = lane_offsets(l);
+    o0 = lo.code0;
+    o1 = lo.code1;
+  } else if (kind == 4) {
+    o0 = 16 * l;
+    o1 = 1024 + 16 * l;
+  } else {
+    o0 = (l & 31) * kVecBytes + 32 * (l >> 5);
+    o1 = o0 + 16;
+  }
+  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = lds_loop(s_img, o0, o1, iters);
+}
+
 }  // namespace
 }  // namespace mqa
 
 extern "C" int32_t mqa_fp4_peak_probe(int32_t kind, float* out, int32_t blocks, int32_t iters, void* stream) {
-  if (kind < 0 || kind > 2 || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
+  if (kind < 0 || kind > 5 || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
   if (out == nullptr) return MQA_ERR_NULL_POINTER;
   if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return MQA_ERR_MISALIGNED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  mqa::peak_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
+  if (kind <= 2)
+    mqa::peak_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
+  else
+    mqa::lds_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
   return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }

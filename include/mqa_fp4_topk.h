@@ -284,7 +284,12 @@ int32_t mqa_fp4_cache_write(const float* k, int64_t n, const int32_t* positions,
  *         4-7 the kind-1 loop, i.e. one wave of each per SIMD (both halves of
  *         the work of kinds 0 and 1): a time near half of kind 0's plus half of
  *         kind 1's means the SIMD runs MFMA and VALU work one after the other,
- *         near the larger half means it overlaps them.
+ *         near the larger half means it overlaps them;
+ * kinds 3-5: LDS read patterns, blocks x 8 waves x iters x 2 ds_read_b128 over
+ *         a 16 KB score-block image: 3 the scan's operand reads (with the chunk
+ *         swizzle), 4 a linear pattern that no bank grouping makes conflict, 5
+ *         the image without a swizzle; kind 3 as fast as kind 4 means the
+ *         image is read free of bank conflicts.
  * out: device float[blocks * 512], written once per lane (keeps the work live).
  * MI355X's published peaks are quoted at 2.4 GHz; timing these launches gives
  * the rates under the clocks the operator actually sees. Returns

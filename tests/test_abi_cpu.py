@@ -93,7 +93,8 @@ def test_stage_event_hook_takes_exactly_five_events(lib):
 
 def test_peak_probe_rejects_bad_arguments_on_host(lib):
     p = ctypes.c_void_p(0x1000)
-    assert lib.mqa_fp4_peak_probe(3, p, 1, 1, None) == -4        # unknown kind
+    assert lib.mqa_fp4_peak_probe(6, p, 1, 1, None) == -4        # unknown kind
+    assert lib.mqa_fp4_peak_probe(-1, p, 1, 1, None) == -4
     assert lib.mqa_fp4_peak_probe(0, p, 0, 1, None) == -4        # no blocks
     assert lib.mqa_fp4_peak_probe(1, p, 1, 0, None) == -4        # no iterations
     assert lib.mqa_fp4_peak_probe(0, None, 1, 1, None) == -2

@@ -215,7 +215,7 @@ def test_peak_probes_run():
     _need_gpu()
     import torch
     out = torch.full((4 * 512,), float("nan"), dtype=torch.float32, device="cuda:0")
-    for kind in (0, 1, 2):
+    for kind in range(6):
         out.fill_(float("nan"))
         mqa.mqa_fp4_peak_probe(kind, out, 4, 8)
         torch.cuda.synchronize()
