@@ -253,14 +253,13 @@ __global__ void __launch_bounds__(1024) decode_gate_kernel(DecArgs a, int mode) 
   if (a.row_state[row] != kRowLong) return;
   const int start = a.row_start[row], end = a.row_end[row];
   const int kp = sample_keep(K, sampled_positions(start, end), end - start);
-  if (threadIdx.x == 0) {
-    int total = 0;
-    for (int i = 0; i < a.splits; ++i) {
-      s_cnt[i] = a.w.sample_n[row * a.splits + i];
-      if (s_cnt[i] < 0) total = -1000000;   // a local selection failed: no gate from this sample
-      total += s_cnt[i];
-    }
-    s_total = total;
+  if (threadIdx.x < 64) {   // splits <= 64: one count per lane
+    const int i = threadIdx.x;
+    const int v = i < a.splits ? a.w.sample_n[row * a.splits + i] : 0;
+    s_cnt[i] = v;
+    const bool failed = __ballot(v < 0) != 0;   // a local selection failed: no gate from this sample
+    const uint32_t total = wave_suffix_sum(static_cast<uint32_t>(max(v, 0)), i);
+    if (i == 0) s_total = failed ? -1 : static_cast<int>(total);
   }
   __syncthreads();
   uint64_t gate = 0;
@@ -271,16 +270,21 @@ __global__ void __launch_bounds__(1024) decode_gate_kernel(DecArgs a, int mode) 
   } else if (mode == 2) {
     gate = ~0ull;                                // nothing passes: underfill, then the fallback
   } else if (s_total > kp) {
+    // every sample slot of the row in registers: slot e = split e / cap, entry e % cap
+    constexpr int E = kMaxDecodeSplits * kDecSampleCap / NT;
     const uint64_t* keys = a.w.samples + static_cast<size_t>(row) * a.splits * kDecSampleCap;
-    auto src = [&](int64_t e, uint64_t& x) -> bool {
-      const int sp = static_cast<int>(e / kDecSampleCap), j = static_cast<int>(e % kDecSampleCap);
-      if (j >= s_cnt[sp]) return false;
-      x = keys[e];
-      return true;
-    };
+    uint64_t x[E];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      const int sp = e / kDecSampleCap;
+      const bool v = sp < a.splits && e % kDecSampleCap < s_cnt[sp];   // sp < 64 as e < 64 * 128
+      x[j] = v ? keys[e] : 0ull;
+      if (v) valid |= 1u << j;
+    }
     bool ok = false;
-    const uint64_t T =
-        block_radix_select<NT, 11>(src, static_cast<int64_t>(a.splits) * kDecSampleCap, kp, s_hist, s_red, &ok);
+    const uint64_t T = block_radix_select_regs<NT, 11, E>(x, valid, kp, s_hist, s_red, &ok);
     if (ok) {
       gate = T - 1;
     } else {
@@ -369,22 +373,13 @@ __global__ void __launch_bounds__(1024) decode_gmerge_kernel(DecArgs a, int32_t*
   const uint64_t* keys = a.w.cand + static_cast<size_t>(row) * a.cap;
   if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
+  constexpr int E = (candidate_cap(K) + NT - 1) / NT;   // every candidate in registers (n <= cap)
+  uint64_t x[E];
+  const uint32_t valid = load_keys_regs<NT, E>(keys, static_cast<int>(n), x);
   bool ok = true;
   uint64_t T = 0;
-  auto src = [&](int64_t i, uint64_t& x) -> bool {
-    x = keys[i];
-    return true;
-  };
-  if (n > static_cast<uint32_t>(K)) T = block_radix_select<NT, 11>(src, static_cast<int64_t>(n), K, s_hist, s_red, &ok);
-  if (ok) {
-    for (int i = threadIdx.x; i < static_cast<int>(n); i += NT) {
-      const uint64_t x = keys[i];
-      if (x >= T) {
-        const int at = atomicAdd(&s_n, 1);
-        if (at < K) s_sel[at] = x;
-      }
-    }
-  }
+  if (n > static_cast<uint32_t>(K)) T = block_radix_select_regs<NT, 11, E>(x, valid, K, s_hist, s_red, &ok);
+  if (ok) gather_at_least<K, E>(x, valid, T, s_sel, &s_n);
   __syncthreads();
   if (!ok || s_n != K) {
     fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, status);

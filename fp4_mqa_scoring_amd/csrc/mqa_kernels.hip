@@ -2,7 +2,7 @@
 //
 // Fused path (all on the caller's stream, no host synchronisation):
 //   row_prep     validate windows and pages, answer short rows (length <= K)
-//   calib        per row: score a sample (every 16th position of the row tile's
+//   calib        per row: score a sample (every 32nd position of the row tile's
 //                range), keep the sample's exact top-k' and derive the gate T0 =
 //                its k'-th key
 //   scan         per (8-row tile, context split): score every 256-position block
@@ -132,21 +132,24 @@ template <int K>
 struct Geometry;
 template <>
 struct Geometry<512> {
-  static constexpr int kCap = 2048;
+  static constexpr int kCap = candidate_cap(512);
   static constexpr int kFbSplits = 4;
 };
 template <>
 struct Geometry<1024> {
-  static constexpr int kCap = 2560;
+  static constexpr int kCap = candidate_cap(1024);
   static constexpr int kFbSplits = 2;
 };
 // Fallback pool per row: all LDS left after the block buffers and histograms.
 constexpr int kPoolCap = 1856;
 constexpr int kFallbackGrid = 256;
 
-// The calibration samples every 16th position. (A stride of 32 halves its cost
-// but the coarser gate sends rows to the exact fallback: measured slower.)
-constexpr int kCalStride = 16;
+// The calibration samples every 32nd position: half the scoring work of a
+// 1/16 sample, and the looser gate (about 32 k' keys pass it) still fits the
+// candidate buffer. Measured at Q = 8192, C4 = 196,608, K = 1024: calibration
+// 0.65 -> 0.37 ms, call 8.45 -> 8.22 ms; with a 2,560-key buffer the same stride
+// overflowed rows into the exact fallback and took 10.4 ms.
+constexpr int kCalStride = 32;
 constexpr int kCalPerPage = kPage / kCalStride;   // sampled positions per page
 static_assert(kCalStride >= 16 && kCalStride <= kPage && kPage % kCalStride == 0, "stride divides the page");
 constexpr int kCalCap = 512;         // calibration pool per row
@@ -238,8 +241,8 @@ struct BlockDma {
 };
 
 // "Sample blocks" of the calibration: sample block v holds the positions
-// base + 16 * (256 v + p), p = 0..255 (base = first position of the row tile's
-// range, a multiple of 256), i.e. every 16th position, four per page. Same LDS
+// base + kCalStride * (256 v + p), p = 0..255 (base = first position of the row
+// tile's range, a multiple of 256), i.e. every 32nd position, two per page. Same LDS
 // image as a score block (position p at slot p, same chunk swizzle), so the
 // block scorer applies unchanged. Every lane copies from its own page.
 struct SampleDma {
@@ -381,8 +384,8 @@ __device__ __forceinline__ uint64_t wave_min_key(const uint64_t* pool, int n, in
 // ---------------------------------------------------------------------------
 // Calibration of the candidate gate ("calibrated candidate filtering", PR 5309
 // Implementation). Per row: exact top-k' of the keys of a sample of its window
-// (every 16th position); the gate is set just below the sample's k'-th key, so
-// that about 16 k' of the window's keys pass it. k' = x + 4 sqrt(x) + 8, where
+// (every kCalStride-th position); the gate is set just below the sample's k'-th
+// key, so that about kCalStride k' of the window's keys pass it. k' = x + 4 sqrt(x) + 8, where
 // x = K m / n is the expected number of the row's top-K among the m sampled
 // positions, makes "fewer than K keys pass" (underfill) a > 4-sigma event; an
 // underfilled row is still exact, it just takes the fallback. Rows whose sample
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
   int u0 = 0, u1 = 0;
   if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
   const int base = u0 * kTile;
-  // sampled positions base + 16 j inside this row's window
+  // sampled positions base + kCalStride j inside this row's window
   const int j_lo = (start - base + kCalStride - 1) / kCalStride;
   const int j_hi = (end - base + kCalStride - 1) / kCalStride;
   const int m = active ? max(0, j_hi - j_lo) : 0;
@@ -999,8 +1002,6 @@ __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restric
 
 static_assert(Geometry<512>::kFbSplits * 512 <= Geometry<512>::kCap, "fallback keys fit the candidate buffer");
 static_assert(Geometry<1024>::kFbSplits * 1024 <= Geometry<1024>::kCap, "fallback keys fit the candidate buffer");
-
-int candidate_cap(int K) { return K == 512 ? Geometry<512>::kCap : Geometry<1024>::kCap; }
 
 // ---------------------------------------------------------------------------
 // Launchers

@@ -70,21 +70,20 @@ __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, BlockScratch<NT
   return v + add;
 }
 
-template <int NT, int DBITS, class Src>
-__device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_t* hist,
-                                       BlockScratch<NT>& s, bool* ok) {
+// Core of the selection: visit(f) calls f(key) for every valid key the calling
+// thread holds.
+template <int NT, int DBITS, class Visit>
+__device__ uint64_t block_radix_select_core(const Visit& visit, int k, uint32_t* hist, BlockScratch<NT>& s,
+                                            bool* ok) {
   constexpr int BINS = 1 << DBITS;
   constexpr int BPT = BINS / NT;  // bins per thread
   static_assert(BPT >= 1 && BINS % NT == 0, "bins must be a multiple of threads");
   const int tid = threadIdx.x;
   uint64_t vor = 0, vand = ~0ull;
-  for (int64_t i = tid; i < n; i += NT) {
-    uint64_t x;
-    if (src(i, x)) {
-      vor |= x;
-      vand &= x;
-    }
-  }
+  visit([&](uint64_t x) {
+    vor |= x;
+    vand &= x;
+  });
   block_or_and<NT>(vor, vand, s);
   if (vor == vand) {   // at most one distinct valid key
     *ok = (k == 1);
@@ -98,11 +97,9 @@ __device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_
     const int shift = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;
     for (int b = tid; b < BINS; b += NT) hist[b] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += NT) {
-      uint64_t x;
-      if (src(i, x) && (x & pmask) == prefix)
-        atomicAdd(&hist[static_cast<uint32_t>(x >> shift) & (BINS - 1)], 1u);
-    }
+    visit([&](uint64_t x) {
+      if ((x & pmask) == prefix) atomicAdd(&hist[static_cast<uint32_t>(x >> shift) & (BINS - 1)], 1u);
+    });
     __syncthreads();
     uint32_t c[BPT];
     uint32_t tsum = 0;
@@ -143,7 +140,62 @@ __device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_
   return prefix;
 }
 
-// Sorts N (power of two) 64-bit values ascending in LDS with NT threads.
+// Keys read through src(i, &key) -> valid, i in [0, n), thread t taking
+// i = t, t + NT, ... (each pass reads them again).
+template <int NT, int DBITS, class Src>
+__device__ uint64_t block_radix_select(const Src& src, int64_t n, int k, uint32_t* hist, BlockScratch<NT>& s,
+                                       bool* ok) {
+  const int tid = threadIdx.x;
+  auto visit = [&](auto&& f) {
+    for (int64_t i = tid; i < n; i += NT) {
+      uint64_t x;
+      if (src(i, x)) f(x);
+    }
+  };
+  return block_radix_select_core<NT, DBITS>(visit, k, hist, s, ok);
+}
+
+// Keys held in registers: x[j] is valid iff bit j of `valid` is set.
+template <int NT, int DBITS, int E>
+__device__ uint64_t block_radix_select_regs(const uint64_t (&x)[E], uint32_t valid, int k, uint32_t* hist,
+                                            BlockScratch<NT>& s, bool* ok) {
+  static_assert(E >= 1 && E <= 32, "validity mask width");
+  auto visit = [&](auto&& f) {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if ((valid >> j) & 1u) f(x[j]);
+  };
+  return block_radix_select_core<NT, DBITS>(visit, k, hist, s, ok);
+}
+
+// Loads keys[i] for i = t + j NT < n into x[j]; returns the validity mask.
+template <int NT, int E>
+__device__ __forceinline__ uint32_t load_keys_regs(const uint64_t* __restrict__ keys, int n, uint64_t (&x)[E]) {
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int i = static_cast<int>(threadIdx.x) + j * NT;
+    x[j] = i < n ? keys[i] : 0ull;
+    if (i < n) valid |= 1u << j;
+  }
+  return valid;
+}
+
+// Appends the keys >= T of x (valid ones) to sel[*n_sel] (LDS, at most K).
+template <int K, int E>
+__device__ __forceinline__ void gather_at_least(const uint64_t (&x)[E], uint32_t valid, uint64_t T, uint64_t* sel,
+                                                int32_t* n_sel) {
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (((valid >> j) & 1u) && x[j] >= T) {
+      const int at = atomicAdd(n_sel, 1);
+      if (at < K) sel[at] = x[j];
+    }
+  }
+}
+
+// Sorts N (power of two) 64-bit values ascending in LDS with NT threads: the
+// bitonic network one compare-exchange per thread pair and barrier per stage.
 template <int N, int NT>
 __device__ __forceinline__ void block_bitonic_sort(uint64_t* v) {
   for (int size = 2; size <= N; size <<= 1) {
@@ -163,6 +215,43 @@ __device__ __forceinline__ void block_bitonic_sort(uint64_t* v) {
   }
 }
 
+// The same network with one value per thread (64 <= N <= NT): thread t < N holds
+// element t in a register; a stride < 64 pairs lanes of one wave (shuffle, no
+// barrier) and only strides >= 64 go through LDS (10 of the 55 stages at
+// N = 1024). Threads t >= N only join the barriers. Measured faster than the
+// LDS network when N <= NT; with several values per thread (256 threads,
+// N = 1024) the shuffles cost more LDS instructions than they save.
+template <int N, int NT>
+__device__ __forceinline__ void block_sort_regs(uint64_t* v) {
+  static_assert(N >= 64 && N <= NT && (N & (N - 1)) == 0, "one value per thread");
+  const int t = threadIdx.x;
+  const bool act = t < N;   // uniform per wave
+  uint64_t x = act ? v[t] : 0ull;
+  // element t keeps the smaller value iff (t is the lower index) == (its run ascends)
+  auto keep = [](uint64_t a, uint64_t b, bool lower, bool up) -> uint64_t {
+    return (lower == up) ? (a < b ? a : b) : (a < b ? b : a);
+  };
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 64) {
+        __syncthreads();   // earlier reads of v are done
+        if (act) v[t] = x;
+        __syncthreads();
+        if (act) x = keep(x, v[t ^ stride], (t & stride) == 0, (t & size) == 0);
+      } else if (act) {
+        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), stride, 64);
+        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), stride, 64);
+        x = keep(x, (static_cast<uint64_t>(hi) << 32) | lo, (t & stride) == 0, (t & size) == 0);
+      }
+    }
+  }
+  __syncthreads();
+  if (act) v[t] = x;
+  __syncthreads();
+}
+
 // Writes one long row's K selected keys (in s_sel) in ascending position order
 // with their physical slots. s_sel is overwritten.
 template <int K, int NT>
@@ -175,7 +264,10 @@ __device__ __forceinline__ void emit_row(uint64_t* s_sel, int64_t row, const int
     s_sel[i] = (static_cast<uint64_t>(key_pos(key)) << 32) | static_cast<uint32_t>(key >> 32);
   }
   __syncthreads();
-  block_bitonic_sort<K, NT>(s_sel);
+  if constexpr (K <= NT)
+    block_sort_regs<K, NT>(s_sel);
+  else
+    block_bitonic_sort<K, NT>(s_sel);
   const size_t base = static_cast<size_t>(row) * K;
   for (int i = threadIdx.x; i < K; i += NT) {
     const uint64_t v = s_sel[i];

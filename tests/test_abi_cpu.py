@@ -149,7 +149,7 @@ def test_decode_entry_checks_arguments_on_host(lib):
     # explicit splits: no device query; O(Q) + Q*splits*(4 + 8K) bytes
     q, K, s = 100, 1024, 5
     a = lambda x: (x + 255) // 256 * 256
-    cap = 2560                                       # candidate keys per row at K = 1024
+    cap = 4096                                       # candidate keys per row at K = 1024
     want = (a(q * 4) + a(q * s * 4) + a(q * s * K * 8) + a(q * s * 128 * 8) + a(q * s * 4) + a(q * 8) + a(q * 4)
             + a(q * cap * 8) + a(q * 4) + a(4))
     assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == want
