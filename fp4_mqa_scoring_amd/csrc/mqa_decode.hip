@@ -14,11 +14,10 @@
 //
 // Pipeline (all on the caller's stream):
 //   row_prep   windows, per-row pages, sequences, short rows
-//   calib      per (row, split) wave: score the row's sampled pages (every 16th
-//              page) and keep the local top-k' sample keys (k' as in the prefill
-//              path's calibration)
-//   gate       per row: the k'-th largest sampled key over all splits is the
-//              row's gate; the candidate count is reset
+//   gate       per row (one block): score the row's sampled pages (every 16th
+//              page) and keep their keys in registers; the k'-th largest (k' as
+//              in the prefill path's calibration) is the row's gate; the
+//              candidate count is reset
 //   scan       per (row, split) wave: every page of the split; keys above the
 //              gate are staged in LDS and appended to the row's bounded buffer
 //   merge      per row: exact top-K of the candidates (if K <= count <= cap),
@@ -163,11 +162,11 @@ __device__ __forceinline__ void split_pages(int start, int end, int split, int s
   *pb = pg0 + static_cast<int>(static_cast<int64_t>(n_pages) * (split + 1) / splits);
 }
 
-// Sampled positions of a window: those in pages whose index is a multiple of 16.
-__device__ __forceinline__ int sampled_positions(int start, int end) {
+// Sampled positions of a window: those in pages whose index is a multiple of
+// `stride`.
+__device__ __forceinline__ int sampled_positions(int start, int end, int stride) {
   int m = 0;
-  for (int pg = (start / kPage + kDecSampleStride - 1) / kDecSampleStride * kDecSampleStride; pg * kPage < end;
-       pg += kDecSampleStride)
+  for (int pg = (start / kPage + stride - 1) / stride * stride; pg * kPage < end; pg += stride)
     m += min(end, (pg + 1) * kPage) - max(start, pg * kPage);
   return m;
 }
@@ -178,113 +177,76 @@ __device__ __forceinline__ int sampled_positions(int start, int end) {
   __shared__ __attribute__((aligned(16))) uint8_t s_s0[kDecWaves][kPageScaleBytes];  \
   __shared__ __attribute__((aligned(16))) uint8_t s_s1[kDecWaves][kPageScaleBytes]
 
-// ---- calibration: local top-k' of the sampled pages ------------------------------
-template <int K>
-__global__ void __launch_bounds__(kDecThreads, 2) decode_calib_kernel(DecArgs a) {
-  constexpr int CAP = 256;
-  MQA_WAVE_PAGES;
-  __shared__ uint64_t s_pool[kDecWaves][CAP];
-  __shared__ uint32_t s_hist[kDecWaves][256];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kDecWaves + wave;
-  if (item >= static_cast<int64_t>(a.Q) * a.splits) return;   // waves are independent: no block barrier below
-  const int row = static_cast<int>(item / a.splits), split = static_cast<int>(item % a.splits);
-  if (a.row_state[row] != kRowLong) return;
-  const int start = a.row_start[row], end = a.row_end[row];
-  const int kp = sample_keep(K, sampled_positions(start, end), end - start);
-  int pa, pb;
-  split_pages(start, end, split, a.splits, &pa, &pb);
-  const int first = (pa + kDecSampleStride - 1) / kDecSampleStride * kDecSampleStride;
-  QRow qr;
-  load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
-            a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
-            a.weights + static_cast<size_t>(row) * kHeads, lane);
-  const LaneOffsets lo = lane_offsets(lane);
-  uint64_t* pool = s_pool[wave];
-  int fill = 0;
-  uint64_t gate = 0;
-  bool failed = false;
-  const int keep = min(kp, kDecSampleCap);
-  stream_pages(a, row_table(a, row), first, pb, kDecSampleStride, WavePages{s_c0[wave], s_s0[wave], s_c1[wave], s_s1[wave]},
-               lane, [&](int pg, const uint8_t* codes, const uint8_t* scales) {
-    const float sc = score_page(qr, codes, scales, lo);
-    const int pos = pg * kPage + lane;
-    const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
-    bool pass = pos >= start && pos < end && key > gate;
-    uint64_t msk = __ballot(pass);
-    if (msk == 0) return;
-    int cnt = __popcll(msk);
-    if (fill + cnt > CAP) {
-      const Selected sel = wave_select_compact(pool, fill, keep, s_hist[wave], lane);
-      if (sel.kept != keep) failed = true;
-      fill = keep;
-      gate = sel.T - 1;
-      pass = pass && key > gate;
-      msk = __ballot(pass);
-      cnt = __popcll(msk);
-    }
-    if (pass) pool[fill + mbcnt64(msk)] = key;
-    fill += cnt;
-  });
-  wave_lds_sync();
-  if (fill > keep) {
-    const Selected sel = wave_select_compact(pool, fill, keep, s_hist[wave], lane);
-    if (sel.kept != keep) failed = true;
-    fill = keep;
-  }
-  uint64_t* dst = a.w.samples + (static_cast<size_t>(row) * a.splits + split) * kDecSampleCap;
-  for (int i = lane; i < fill; i += 64) dst[i] = pool[i];
-  if (lane == 0) a.w.sample_n[static_cast<size_t>(row) * a.splits + split] = failed ? kCodeSelector : fill;
-}
-
-// ---- gate per row -------------------------------------------------------------------
+// ---- calibration and gate per row ---------------------------------------------------
+// One 1024-thread block per long row. Its 16 waves score the row's sampled pages
+// (index a multiple of the sample stride), wave w taking sampled pages w, w + 16,
+// ..., each streamed through the wave's two LDS page buffers; every lane keeps
+// the key of its position of each page in a register (0 = no key: a real key's
+// low word is ~position, never 0). The block's exact radix select over those
+// registers gives the k'-th largest sampled key, and the gate just below it.
+// The stride is 16 pages, or on windows of more than 16 * 16 * kDecGateRegs
+// pages (131,072 positions) the multiple of 16 that keeps the sample within
+// 16 * kDecGateRegs pages; any gate keeps the result exact, a coarser one only
+// lets more candidates through.
 // mode 0: gate from the sample; 1: every long row to the exact fallback (no
 // prefilter); 2: gate above every key (forced underfill, then the fallback).
-// One 1024-thread block per long row, 11-bit digits (few blocks: decode batches
-// are small, so each one should finish in few passes).
+constexpr int kDecGateWaves = 16;
+constexpr int kDecGateRegs = 8;   // sampled pages per wave
+
 template <int K>
-__global__ void __launch_bounds__(1024) decode_gate_kernel(DecArgs a, int mode) {
-  constexpr int NT = 1024;
+__global__ void __launch_bounds__(kDecGateWaves * 64) decode_gate_kernel(DecArgs a, int mode) {
+  constexpr int NT = kDecGateWaves * 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_c0[kDecGateWaves][kPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_c1[kDecGateWaves][kPageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_s0[kDecGateWaves][kPageScaleBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_s1[kDecGateWaves][kPageScaleBytes];
   __shared__ uint32_t s_hist[2048];
-  __shared__ int32_t s_cnt[kMaxDecodeSplits];
   __shared__ BlockScratch<NT> s_red;
-  __shared__ int32_t s_total;
-  const int64_t row = blockIdx.x;
+  const int row = blockIdx.x;
   if (a.row_state[row] != kRowLong) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int start = a.row_start[row], end = a.row_end[row];
-  const int kp = sample_keep(K, sampled_positions(start, end), end - start);
-  if (threadIdx.x < 64) {   // splits <= 64: one count per lane
-    const int i = threadIdx.x;
-    const int v = i < a.splits ? a.w.sample_n[row * a.splits + i] : 0;
-    s_cnt[i] = v;
-    const bool failed = __ballot(v < 0) != 0;   // a local selection failed: no gate from this sample
-    const uint32_t total = wave_suffix_sum(static_cast<uint32_t>(max(v, 0)), i);
-    if (i == 0) s_total = failed ? -1 : static_cast<int>(total);
-  }
-  __syncthreads();
+  const int pg0 = start / kPage, pg1 = (end - 1) / kPage + 1;   // the window's pages [pg0, pg1)
+  // L pages hold at most ceil(L / s) multiples of s: this stride leaves at most
+  // B = 16 * kDecGateRegs sampled pages (16 up to 16 B pages).
+  constexpr int kBudget = kDecGateWaves * kDecGateRegs;
+  const int L = pg1 - pg0;
+  const int stride = kDecSampleStride * max(1, (L + kDecSampleStride * kBudget - 1) / (kDecSampleStride * kBudget));
+  const int m = sampled_positions(start, end, stride);
+  const int kp = sample_keep(K, m, end - start);
   uint64_t gate = 0;
   uint32_t count = 0;
-  if (mode == 1 || s_total < 0) {
+  if (mode == 1) {
     gate = ~0ull;
     count = static_cast<uint32_t>(a.cap) + 1;   // overflow marker: exact fallback
   } else if (mode == 2) {
     gate = ~0ull;                                // nothing passes: underfill, then the fallback
-  } else if (s_total > kp) {
-    // every sample slot of the row in registers: slot e = split e / cap, entry e % cap
-    constexpr int E = kMaxDecodeSplits * kDecSampleCap / NT;
-    const uint64_t* keys = a.w.samples + static_cast<size_t>(row) * a.splits * kDecSampleCap;
-    uint64_t x[E];
+  } else if (m > kp) {
+    QRow qr;
+    load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
+              a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
+              a.weights + static_cast<size_t>(row) * kHeads, lane);
+    const LaneOffsets lo = lane_offsets(lane);
+    uint64_t x[kDecGateRegs];
+#pragma unroll
+    for (int j = 0; j < kDecGateRegs; ++j) x[j] = 0ull;
+    const int first = (pg0 + stride - 1) / stride * stride + stride * wave;
+    stream_pages(a, row_table(a, row), first, pg1, stride * kDecGateWaves,
+                 WavePages{s_c0[wave], s_s0[wave], s_c1[wave], s_s1[wave]}, lane,
+                 [&](int pg, const uint8_t* codes, const uint8_t* scales) {
+      const float sc = score_page(qr, codes, scales, lo);
+      const int pos = pg * kPage + lane;
+      // shift register: the newest key enters at the top (static register names)
+#pragma unroll
+      for (int j = 0; j + 1 < kDecGateRegs; ++j) x[j] = x[j + 1];
+      x[kDecGateRegs - 1] = (pos >= start && pos < end) ? make_key(sc, static_cast<uint32_t>(pos)) : 0ull;
+    });
     uint32_t valid = 0;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      const int sp = e / kDecSampleCap;
-      const bool v = sp < a.splits && e % kDecSampleCap < s_cnt[sp];   // sp < 64 as e < 64 * 128
-      x[j] = v ? keys[e] : 0ull;
-      if (v) valid |= 1u << j;
-    }
+    for (int j = 0; j < kDecGateRegs; ++j)
+      if (x[j] != 0ull) valid |= 1u << j;
     bool ok = false;
-    const uint64_t T = block_radix_select_regs<NT, 11, E>(x, valid, kp, s_hist, s_red, &ok);
+    const uint64_t T = block_radix_select_regs<NT, 11, kDecGateRegs>(x, valid, kp, s_hist, s_red, &ok);
     if (ok) {
       gate = T - 1;
     } else {
@@ -526,8 +488,7 @@ void launch_decode_k(const DecArgs& a, const PathArgs& p, int mode, int32_t* sta
   const dim3 rgrid(static_cast<unsigned>(p.Q));
   const int64_t fb_cap = (items + kDecWaves - 1) / kDecWaves;
   const dim3 fgrid(static_cast<unsigned>(fb_cap < kDecFallbackBlocks ? fb_cap : kDecFallbackBlocks));
-  decode_calib_kernel<K><<<sgrid, dim3(kDecThreads), 0, st>>>(a);
-  decode_gate_kernel<K><<<rgrid, dim3(1024), 0, st>>>(a, mode);
+  decode_gate_kernel<K><<<rgrid, dim3(kDecGateWaves * 64), 0, st>>>(a, mode);
   if (mark) mark(2, st);   // before the gated scan
   decode_gscan_kernel<K><<<sgrid, dim3(kDecThreads), 0, st>>>(a);
   if (mark) mark(3, st);   // after it
@@ -544,10 +505,9 @@ size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits) {
   const size_t q = static_cast<size_t>(Q), s = static_cast<size_t>(splits);
   const size_t cap = static_cast<size_t>(candidate_cap(K));
   return align256(q * sizeof(int32_t)) + align256(q * s * sizeof(int32_t)) +
-         align256(q * s * static_cast<size_t>(K) * sizeof(uint64_t)) +
-         align256(q * s * kDecSampleCap * sizeof(uint64_t)) + align256(q * s * sizeof(int32_t)) +
-         align256(q * sizeof(uint64_t)) + align256(q * sizeof(uint32_t)) + align256(q * cap * sizeof(uint64_t)) +
-         align256(q * sizeof(int32_t)) + align256(sizeof(int32_t));
+         align256(q * s * static_cast<size_t>(K) * sizeof(uint64_t)) + align256(q * sizeof(uint64_t)) +
+         align256(q * sizeof(uint32_t)) + align256(q * cap * sizeof(uint64_t)) + align256(q * sizeof(int32_t)) +
+         align256(sizeof(int32_t));
 }
 
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits) {
@@ -563,8 +523,6 @@ DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t sp
   w.row_state = reinterpret_cast<int32_t*>(take(q * sizeof(int32_t)));
   w.counts = reinterpret_cast<int32_t*>(take(q * s * sizeof(int32_t)));
   w.keys = reinterpret_cast<uint64_t*>(take(q * s * static_cast<size_t>(K) * sizeof(uint64_t)));
-  w.samples = reinterpret_cast<uint64_t*>(take(q * s * kDecSampleCap * sizeof(uint64_t)));
-  w.sample_n = reinterpret_cast<int32_t*>(take(q * s * sizeof(int32_t)));
   w.gate = reinterpret_cast<uint64_t*>(take(q * sizeof(uint64_t)));
   w.cand_n = reinterpret_cast<uint32_t*>(take(q * sizeof(uint32_t)));
   w.cand = reinterpret_cast<uint64_t*>(take(q * cap * sizeof(uint64_t)));

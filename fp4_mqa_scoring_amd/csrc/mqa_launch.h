@@ -64,8 +64,6 @@ struct DecodeScratch {
   int32_t* row_state;   // [Q]
   int32_t* counts;      // [Q, splits]      fallback: keys per (row, split)
   uint64_t* keys;       // [Q, splits, K]   fallback: top-K per (row, split)
-  uint64_t* samples;    // [Q, splits, kDecSampleCap] calibration keys
-  int32_t* sample_n;    // [Q, splits]
   uint64_t* gate;       // [Q]
   uint32_t* cand_n;     // [Q]              candidates appended (may exceed cap: overflow)
   uint64_t* cand;       // [Q, candidate_cap(K)]
@@ -73,7 +71,6 @@ struct DecodeScratch {
   int32_t* fb_count;    // [1]              (cleared by row_prep)
 };
 constexpr int kMaxDecodeSplits = 64;
-constexpr int kDecSampleCap = 128;   // calibration keys kept per (row, split); k' <= 104
 size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
 // Measurement marker called between launches (index, stream); may be null.

@@ -223,9 +223,10 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
  * The call allocates nothing, never synchronises and accepts a capturing
  * stream; row failures are reported in out_count and the sticky status word
  * only (read mqa_fp4_status outside the graph). Each row is scanned
- * independently (no key sharing between rows), one wave per (row, split): a
- * calibrated gate from every 16th page (PR 5309's calibrated candidate filter),
- * a gated scan into a bounded per-row candidate buffer and an exact merge; rows
+ * independently (no key sharing between rows): a calibrated gate per row from
+ * every 16th page (PR 5309's calibrated candidate filter; a coarser multiple of
+ * 16 on windows beyond 131,072 positions), then one wave per (row, split) for a
+ * gated scan into a bounded per-row candidate buffer and an exact merge; rows
  * that underfill or overflow are recomputed exactly by per-wave bounded LDS
  * pools (PR 5282's streaming design) with an exact merge of the splits. flags:
  * MQA_FLAG_NO_PREFILTER or MQA_FLAG_FORCE_UNDERFILL (for tests; the split bits

@@ -150,6 +150,6 @@ def test_decode_entry_checks_arguments_on_host(lib):
     q, K, s = 100, 1024, 5
     a = lambda x: (x + 255) // 256 * 256
     cap = 4096                                       # candidate keys per row at K = 1024
-    want = (a(q * 4) + a(q * s * 4) + a(q * s * K * 8) + a(q * s * 128 * 8) + a(q * s * 4) + a(q * 8) + a(q * 4)
-            + a(q * cap * 8) + a(q * 4) + a(4))
+    want = (a(q * 4) + a(q * s * 4) + a(q * s * K * 8) + a(q * 8) + a(q * 4) + a(q * cap * 8) + a(q * 4)
+            + a(4))
     assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == want
