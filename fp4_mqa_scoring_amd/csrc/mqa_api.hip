@@ -489,12 +489,12 @@ int64_t mqa_fp4_tiled_scratch_bytes(int64_t num_rows, int32_t K, int32_t tile_po
                               align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float)));
 }
 
-// Context splits of the decode path: enough (row, split) waves for three
-// 4-wave CTAs per CU (on a 64-row batch of 32K..131K-position contexts, 16,
-// 24, 32, 48 and 64 splits took 0.190, 0.157, 0.144, 0.137 and 0.147 ms).
+// Context splits of the decode path: enough (row, split) waves to fill the
+// four 4-wave scan blocks that fit per CU (on a 64-row batch of 32K..131K-
+// position contexts, 32, 48 and 64 splits took 0.136, 0.127 and 0.125 ms).
 static int32_t decode_splits(int64_t Q, int cus, int32_t requested) {
   if (requested > 0) return requested;
-  const int64_t target = 12ll * cus;
+  const int64_t target = 16ll * cus;
   int64_t s = (target + Q - 1) / (Q > 0 ? Q : 1);
   if (s < 1) s = 1;
   if (s > mqa::kMaxDecodeSplits) s = mqa::kMaxDecodeSplits;

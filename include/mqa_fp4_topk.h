@@ -224,8 +224,8 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
  * stream; row failures are reported in out_count and the sticky status word
  * only (read mqa_fp4_status outside the graph). Each row is scanned
  * independently (no key sharing between rows): a calibrated gate per row from
- * every 16th page (PR 5309's calibrated candidate filter; a coarser multiple of
- * 16 on windows beyond 131,072 positions), then one wave per (row, split) for a
+ * every 32nd page (PR 5309's calibrated candidate filter; a coarser multiple of
+ * 32 on windows beyond 262,144 positions), then one wave per (row, split) for a
  * gated scan into a bounded per-row candidate buffer and an exact merge; rows
  * that underfill or overflow are recomputed exactly by per-wave bounded LDS
  * pools (PR 5282's streaming design) with an exact merge of the splits. flags:
