@@ -344,6 +344,33 @@ def test_empty_batch_is_a_no_op():
     assert raw.shape == (0, 512) and cnt.shape == (0,)
 
 
+def test_empty_inputs_are_no_ops_on_every_entry_point():
+    """Zero rows (tiled, decode), zero vectors (quantiser, cache writer): the call
+    succeeds, launches nothing that writes, and leaves the status clear."""
+    _need_gpu()
+    import torch
+    inp = synth.make_inputs(0, 512, 512, 3)
+    t = gu.to_device(inp)
+    outs = mqa.alloc_outputs(0, 1024, "cuda")
+    mqa.mqa_fp4_tiled_topk_prefill(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], t["page_table"],
+                                   t["row_start"], t["row_end"], 1024, *outs)
+    assert mqa.mqa_fp4_decode_workspace_bytes(0, 1024, 0) >= 0
+    ws = torch.empty(max(mqa.mqa_fp4_decode_workspace_bytes(0, 1024, 0), 1), dtype=torch.uint8, device="cuda")
+    bt = torch.zeros((1, 8), dtype=torch.int32, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    mqa.mqa_fp4_topk_decode(t["q"], t["q_scale"], t["k_pages"], t["k_scale"], t["weights"], bt, none, none, none,
+                            1024, *outs, ws)
+    codes, scales = mqa.mqa_fp4_quantize(torch.empty((0, 128), dtype=torch.float32, device="cuda"))
+    assert codes.shape == (0, 64) and scales.shape == (0, 4)
+    kp = torch.full((2, 64, 64), 0x5A, dtype=torch.uint8, device="cuda")
+    ks = torch.full((2, 64, 4), 0x7F, dtype=torch.uint8, device="cuda")
+    mqa.mqa_fp4_cache_write(torch.empty((0, 128), dtype=torch.float32, device="cuda"), none,
+                            torch.arange(2, dtype=torch.int32, device="cuda"), kp, ks)
+    torch.cuda.synchronize()
+    assert bool((kp == 0x5A).all()) and bool((ks == 0x7F).all())
+    assert mqa.mqa_fp4_status() == 0
+
+
 # --- special values -------------------------------------------------------------------------
 
 def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
