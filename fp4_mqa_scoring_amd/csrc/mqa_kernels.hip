@@ -153,7 +153,6 @@ constexpr int kCalStride = 32;
 constexpr int kCalPerPage = kPage / kCalStride;   // sampled positions per page
 static_assert(kCalStride >= 16 && kCalStride <= kPage && kPage % kCalStride == 0, "stride divides the page");
 constexpr int kCalCap = 512;         // calibration pool per row
-constexpr int kStageCap = 256;       // per-wave LDS staging of candidate keys
 
 // Score blocks [a, a+n) visited by a CTA.
 struct BlockSeq {
@@ -342,6 +341,56 @@ __device__ __forceinline__ void stream_dma(const ScanArgs& a, const Dma& d, cons
   }
 }
 
+// One step of the paired stream: start the copies of blocks i+2 and i+3 into
+// the other pair of buffers, score blocks i and i+1, then wait for the copies
+// and for every wave (one barrier per two blocks).
+template <class Dma, class Body>
+__device__ __forceinline__ void stream_pair_step(const ScanArgs& a, const BlockSeq& seq, const Dma& d,
+                                                 typename Dma::Ent& ent0, typename Dma::Ent& ent1, int i, int lane,
+                                                 const uint8_t* c0, const uint8_t* s0, const uint8_t* c1,
+                                                 const uint8_t* s1, uint8_t* nc0, uint8_t* ns0, uint8_t* nc1,
+                                                 uint8_t* ns1, Body& body) {
+  if (i + 2 < seq.n) {
+    d.issue(a, ent0, nc0, ns0, lane);
+    if (i + 4 < seq.n) ent0 = d.entries(a, seq.tile(i + 4), lane);
+  }
+  if (i + 3 < seq.n) {
+    d.issue(a, ent1, nc1, ns1, lane);
+    if (i + 5 < seq.n) ent1 = d.entries(a, seq.tile(i + 5), lane);
+  }
+  body(seq.tile(i), c0, s0);
+  if (i + 1 < seq.n) body(seq.tile(i + 1), c1, s1);
+  vm_wait_all();
+  __syncthreads();
+}
+
+// Streams the blocks of seq two at a time through four LDS buffers (pairs A
+// and B, every access named statically as in stream_dma): half the barriers
+// of the single-block stream.
+template <class Body>
+__device__ __forceinline__ void stream_block_pairs(const ScanArgs& a, const BlockSeq& seq, uint8_t* ca0, uint8_t* sa0,
+                                                   uint8_t* ca1, uint8_t* sa1, uint8_t* cb0, uint8_t* sb0,
+                                                   uint8_t* cb1, uint8_t* sb1, Body&& body) {
+  if (seq.n <= 0) return;
+  BlockDma d;
+  d.init(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+  const int lane = threadIdx.x & 63;
+  BlockDma::Ent ent0 = d.entries(a, seq.tile(0), lane);
+  BlockDma::Ent ent1 = seq.n > 1 ? d.entries(a, seq.tile(1), lane) : ent0;
+  vm_wait_all();
+  d.issue(a, ent0, ca0, sa0, lane);
+  if (seq.n > 1) d.issue(a, ent1, ca1, sa1, lane);
+  if (seq.n > 2) ent0 = d.entries(a, seq.tile(2), lane);
+  if (seq.n > 3) ent1 = d.entries(a, seq.tile(3), lane);
+  vm_wait_all();
+  __syncthreads();
+  for (int i = 0; i < seq.n; i += 4) {
+    stream_pair_step(a, seq, d, ent0, ent1, i, lane, ca0, sa0, ca1, sa1, cb0, sb0, cb1, sb1, body);
+    if (i + 2 < seq.n)
+      stream_pair_step(a, seq, d, ent0, ent1, i + 2, lane, cb0, sb0, cb1, sb1, ca0, sa0, ca1, sa1, body);
+  }
+}
+
 template <class Body>
 __device__ __forceinline__ void stream_blocks(const ScanArgs& a, const BlockSeq& seq, uint8_t* codes0, uint8_t* scales0,
                                               uint8_t* codes1, uint8_t* scales1, Body&& body) {
@@ -500,8 +549,15 @@ template <int K>
 // Four waves per SIMD (the second launch bound is a minimum of waves per SIMD):
 // two CTAs per CU, at most 128 VGPRs.
 __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandArgs c) {
+  // Four block buffers (two pairs) and 128 staged keys per wave: 77,824 B, so
+  // two CTAs still fit per CU.
+  constexpr int kScanStage = 128;
   MQA_BLOCK_BUFFERS;
-  __shared__ uint64_t s_stage[kRowsPerCta][kStageCap];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes2[kTile * kVecBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes3[kTile * kVecBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales2[kTile * kVecScales];
+  __shared__ __attribute__((aligned(16))) uint8_t s_scales3[kTile * kVecScales];
+  __shared__ uint64_t s_stage[kRowsPerCta][kScanStage];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -544,7 +600,8 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
     sf = 0;
   };
   const LaneOffsets lo = lane_offsets(lane);
-  stream_blocks(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, [&](int t, const uint8_t* codes, const uint8_t* scales) {
+  stream_block_pairs(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, s_codes2, s_scales2, s_codes3, s_scales3,
+                     [&](int t, const uint8_t* codes, const uint8_t* scales) {
     if (!active) return;
     const int tb = t * kTile;
     if (tb >= end || tb + kTile <= start) return;
@@ -559,7 +616,7 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
       msk &= __ballot(key > gate);
       if (msk == 0) return;
       const int cnt = __popcll(msk);
-      if (sf + cnt > kStageCap) flush();
+      if (sf + cnt > kScanStage) flush();
       if ((msk >> lane) & 1ull) stage[sf + mbcnt64(msk)] = key;
       sf += cnt;
     });
