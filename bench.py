@@ -320,8 +320,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the operator "
-              "shards by rows with no exchange, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the operator shards by rows "
+              "with no exchange between GPUs, so N GPUs would run N independent row slices", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -26,7 +26,7 @@ Layout of one input set (all numpy, C-contiguous):
   row_start  int32   [Q]           window [start, end) in C4 positions
   row_end    int32   [Q]
 
-Value recipe (stated in the design doc): codes uniform over all 16 E2M1 codes,
+Value recipe: codes uniform over all 16 E2M1 codes,
 scale bytes 127 + U{-2..2}, weights N(0, 1/64) rounded to float32, page table a
 seeded permutation, 5% of key positions duplicated (codes and scales) from a
 seeded earlier, non-duplicated position.

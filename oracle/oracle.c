@@ -28,7 +28,7 @@
  * block scale products span less than 2^38 (the generator's exponents, in
  * [-2, 2] per operand, span 2^8). Wider spreads round once per block add.
  *
- * Readings where the pages are silent (listed in the design doc as well):
+ * Readings where the pages are silent:
  *  - element 2j of a packed vector is the low nibble of byte j;
  *  - a UE8M0 byte e scales by 2^(e-127); the byte 0xFF decodes to NaN
  *    (out of contract, parity unpinned);
@@ -274,7 +274,7 @@ int oracle_max_threads(void) {
  *   3. every element is V_i / X rounded to the nearest E2M1 value, a tie going
  *      to the code whose mantissa bit is 0, magnitudes beyond 6 saturating to 6,
  *      and the sign kept (a negative value that rounds to zero is -0, code 8).
- * Readings where that rule leaves the encoding open (listed in the design doc):
+ * Readings where that rule leaves the encoding open:
  *   - the scale byte is shared + 127, clamped to [0, 254];
  *   - a block whose elements are all zero gets scale byte 0 and the zero codes
  *     of their signs;
