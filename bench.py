@@ -304,7 +304,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="H", help="H (headline) or 1..5")
+    ap.add_argument("--workload", default="H",
+                    help="H (headline), 1..5, or another shape of the pages' Validation table: "
+                         "F65, F131, F196 (V4-Flash, K=512), P65, P131 (V4-Pro, K=1024)")
     ap.add_argument("--pairs", type=int, default=15, help="alternating dense/fused pairs (0 = skip dense)")
     ap.add_argument("--tiled-pairs", type=int, default=5,
                     help="alternating context-tiled/fused pairs (0 = skip the tiled comparator)")
@@ -349,7 +351,9 @@ def main():
     if args.op == "decode":
         bench_decode(args, torch, mqa, dev)
         return
-    cfg = args.workload if args.workload == "H" else int(args.workload)
+    cfg = int(args.workload) if args.workload.isdigit() else args.workload
+    if cfg not in synth.CONFIGS:
+        sys.exit(f"bench.py: unknown workload {args.workload!r} (H, 1..5, F65, F131, F196, P65, P131)")
     inp = synth.make_config(cfg)
     Q, S, K = inp.Q, inp.S, inp.K
     pairs = inp.scored_pairs()
@@ -534,7 +538,7 @@ def main():
         "checks_ok": ok,
     }
     key = (Q, S, K)
-    if key in PAGES_LITETOPK_MS and args.workload == "H":
+    if key in PAGES_LITETOPK_MS:   # the pages' LiteTopK at this exact shape
         line["vs_baseline"] = PAGES_LITETOPK_MS[key] / ms_step
     if args.cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, seed=1)

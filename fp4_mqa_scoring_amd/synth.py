@@ -190,11 +190,20 @@ CONFIGS = {
     5: dict(Q=8192, S=262144, K=1024, name="V4-Pro long prefill Q=8192 C4=262144 K=1024"),
     # headline shape of the pages' Validation table (V4-Pro, 786,432 raw tokens)
     "H": dict(Q=8192, S=196608, K=1024, name="V4-Pro headline Q=8192 C4=196608 K=1024"),
+    # the table's other shapes ("[FlyDSL] Add FP4 LiteTopK prefill operator",
+    # Validation): V4-Flash (K=512) and V4-Pro (K=1024) at 262,144 / 524,288 /
+    # 786,432 raw tokens, i.e. C4 65,536 / 131,072 / 196,608, Q = 8192
+    "F65": dict(Q=8192, S=65536, K=512, name="V4-Flash Q=8192 C4=65536 K=512"),
+    "F131": dict(Q=8192, S=131072, K=512, name="V4-Flash Q=8192 C4=131072 K=512"),
+    "F196": dict(Q=8192, S=196608, K=512, name="V4-Flash Q=8192 C4=196608 K=512"),
+    "P65": dict(Q=8192, S=65536, K=1024, name="V4-Pro Q=8192 C4=65536 K=1024"),
+    "P131": dict(Q=8192, S=131072, K=1024, name="V4-Pro Q=8192 C4=131072 K=1024"),
 }
+_NAMED_IDS = {"H": 6, "F65": 7, "F131": 8, "F196": 9, "P65": 10, "P131": 11}
 
 
 def config_seed(cfg) -> int:
-    cid = 6 if cfg == "H" else int(cfg)
+    cid = _NAMED_IDS[cfg] if isinstance(cfg, str) else int(cfg)
     return BASE_SEED + 1000 * cid
 
 
