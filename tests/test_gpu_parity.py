@@ -385,20 +385,26 @@ def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
     check_rows(inp, range(8), raw, slot, cnt, None, where="special weights")
 
 
-def test_logits_selector_total_order_on_special_value_arrays():
+@pytest.mark.parametrize("S,lo,hi", [(2048, 300, 1600), (40960, 9000, 40000)])
+def test_logits_selector_total_order_on_special_value_arrays(S, lo, hi):
     """Exact TopK over caller logits mixing NaN, +-inf, +-0 and ties: must equal
-    the oracle's selection exactly (no tolerance; the logits are given)."""
+    the oracle's selection exactly (no tolerance; the logits are given). Short
+    windows take the multi-pass select; windows of 8,192 positions or more take
+    the sampled gate and the LDS candidate pass (a row of equal values and a row
+    of NaNs among them)."""
     _need_gpu()
     import torch
-    rng = np.random.default_rng(17)
-    Q, S = 12, 2048
+    rng = np.random.default_rng(17 + S)
+    Q = 12
     pool = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 2.5, 1e-30, -1e-30, 3e38], np.float32)
     lg = pool[rng.integers(0, pool.size, (Q, S))]
     lg[::3] = np.where(rng.random((4, S)) < 0.5, lg[::3], rng.standard_normal((4, S)).astype(np.float32))
     nanpay = np.array([0x7FC00001, 0xFFC00000, 0x7F800001], np.uint32).view(np.float32)
     lg[5, ::7] = nanpay[rng.integers(0, 3, lg[5, ::7].shape)]
+    lg[7] = 1.0                                            # every key tied on the score
+    lg[8] = np.where(rng.random(S) < 0.9, np.float32(np.nan), lg[8])
     st = rng.integers(0, 600, Q).astype(np.int32)
-    en = np.minimum(st + rng.integers(300, 1600, Q), S).astype(np.int32)
+    en = np.minimum(st + rng.integers(lo, hi, Q), S).astype(np.int32)
     pt = rng.permutation(S // 64).astype(np.int32)
     for K in (512, 1024):
         outs = mqa.alloc_outputs(Q, K, "cuda", with_score=True)
