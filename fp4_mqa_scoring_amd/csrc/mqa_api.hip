@@ -456,23 +456,25 @@ int32_t mqa_fp4_tiled_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   const size_t Qz = static_cast<size_t>(num_rows);
   const size_t state_b = align_up(Qz * sizeof(int32_t));
   const size_t count_b = align_up(Qz * sizeof(int32_t));
-  const size_t run_b = align_up(Qz * static_cast<size_t>(K) * sizeof(uint64_t));
+  const size_t floor_b = align_up(Qz * sizeof(uint64_t));
+  const size_t run_b = align_up(Qz * static_cast<size_t>(mqa::tile_pool_cap(K)) * sizeof(uint64_t));
   const size_t tile_b = align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float));
   Scratch scratch;
-  rc = scratch.alloc(state_b + count_b + run_b + tile_b, st);
+  rc = scratch.alloc(state_b + count_b + floor_b + run_b + tile_b, st);
   if (rc != MQA_OK) return rc;
   char* base = static_cast<char*>(scratch.p);
   int32_t* row_state = reinterpret_cast<int32_t*>(base);
   int32_t* run_count = reinterpret_cast<int32_t*>(base + state_b);
-  uint64_t* running = reinterpret_cast<uint64_t*>(base + state_b + count_b);
-  float* tile_logits = reinterpret_cast<float*>(base + state_b + count_b + run_b);
+  uint64_t* run_floor = reinterpret_cast<uint64_t*>(base + state_b + count_b);
+  uint64_t* running = reinterpret_cast<uint64_t*>(base + state_b + count_b + floor_b);
+  float* tile_logits = reinterpret_cast<float*>(base + state_b + count_b + floor_b + run_b);
   record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   record_stage(1, st);
   record_stage(2, st);
   if (rc == MQA_OK)
     rc = hip_rc(mqa::launch_tiled(p, row_state, auto_splits(num_rows, info.cus), tile_positions, tile_logits,
-                                  running, run_count, st));
+                                  running, run_count, run_floor, st));
   record_stage(3, st);
   record_stage(4, st);
   return rc;
@@ -484,8 +486,8 @@ int64_t mqa_fp4_tiled_scratch_bytes(int64_t num_rows, int32_t K, int32_t tile_po
   if (num_rows < 0 || tile_positions < 0 || tile_positions % 256 != 0 || tile_positions > (1 << 22))
     return MQA_ERR_BAD_SIZE;
   const size_t Qz = static_cast<size_t>(num_rows);
-  return static_cast<int64_t>(2 * align_up(Qz * sizeof(int32_t)) +
-                              align_up(Qz * static_cast<size_t>(K) * sizeof(uint64_t)) +
+  return static_cast<int64_t>(2 * align_up(Qz * sizeof(int32_t)) + align_up(Qz * sizeof(uint64_t)) +
+                              align_up(Qz * static_cast<size_t>(mqa::tile_pool_cap(K)) * sizeof(uint64_t)) +
                               align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float)));
 }
 

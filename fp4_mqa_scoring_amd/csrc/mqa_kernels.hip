@@ -1012,24 +1012,33 @@ __global__ void __launch_bounds__(1024, 8) logits_topk_kernel(
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
 }
 
-// Gated candidate buffer per row, and the fallback's pool and splits.
 // ---------------------------------------------------------------------------
 // Bounded context-tiled exact TopK ("[FlyDSL][DSv4] Prototype FP4 MQA streaming
 // TopK", Changes: besides the fused operator the pages keep an exact path whose
 // memory is bounded by tiling the context, for correctness checks and as a
 // reference). The context is visited in tiles of `tile` positions; the
 // dense scorer writes one tile's fp32 scores of every row into a [Q, tile]
-// buffer, then each row merges its running exact top-K (at most K keys, same
-// total order) with the tile's keys by an exact radix select. Every position of
-// a window is seen in exactly one tile, so after the last tile the running set
-// is the window's top-K. No gate, no calibration; scratch Q * (4 tile + 8 K)
-// bytes, independent of the context length.
+// buffer, then each row merges the tile into its pool. A row's pool holds at
+// most tile_pool_cap(K) keys and a floor: no key at or below the floor can be
+// among the row's top K (K pool keys are above it). The tile's keys above the
+// floor are appended to the pool; when the pool would overflow, pool and tile
+// keys are compacted to their top K by an exact radix select and the floor
+// rises to the K-th key. Every position of a window is seen in exactly one
+// tile, so after the last tile the pool's top K is the window's. The K-th key
+// of the first t tiles leaves about K / t keys of the next tile above it, so a
+// row compacts about K ln(tiles) / K times and most tiles cost one read of
+// their logits. No gate, no calibration; scratch
+// Q (4 tile + 8 tile_pool_cap(K) + 16) bytes, independent of the context length.
 // ---------------------------------------------------------------------------
-constexpr int kTileNewCap = 1024;   // tile keys above the running minimum held in LDS
+constexpr int kTileNewCap = 1024;   // tile keys above the floor gathered in LDS
 
-__global__ void __launch_bounds__(256) tile_reset_kernel(int32_t* __restrict__ run_count, int64_t Q) {
+__global__ void __launch_bounds__(256) tile_reset_kernel(int32_t* __restrict__ run_count,
+                                                         uint64_t* __restrict__ run_floor, int64_t Q) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i < Q) run_count[i] = 0;
+  if (i < Q) {
+    run_count[i] = 0;
+    run_floor[i] = 0ull;   // every key is above 0 (its low word is ~position)
+  }
 }
 
 template <int K>
@@ -1037,125 +1046,154 @@ __global__ void __launch_bounds__(256) tile_merge_kernel(const int32_t* __restri
                                                          const int32_t* __restrict__ row_start,
                                                          const int32_t* __restrict__ row_end,
                                                          const float* __restrict__ tile_logits, int32_t tile,
-                                                         int32_t lo, int32_t hi, uint64_t* __restrict__ running,
-                                                         int32_t* __restrict__ run_count) {
+                                                         int32_t lo, int32_t hi, uint64_t* __restrict__ pool,
+                                                         int32_t* __restrict__ run_count,
+                                                         uint64_t* __restrict__ run_floor) {
   constexpr int NT = 256;
-  __shared__ uint64_t s_run[K];
+  constexpr int CAP = tile_pool_cap(K);
+  __shared__ uint64_t s_pool[CAP];
   __shared__ uint64_t s_new[kTileNewCap];
   __shared__ uint32_t s_hist[256];
   __shared__ BlockScratch<NT> s_red;
   __shared__ int32_t s_n, s_m;
-  __shared__ uint64_t s_min;
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
   const int32_t a = max(row_start[row], lo), b = min(row_end[row], hi);
   if (a >= b) return;
-  const int n_run = run_count[row];
+  const int c = run_count[row];
+  if (c < 0) return;   // an earlier compaction failed: the emit fails the row closed
+  const uint64_t floor_key = run_floor[row];
   const int n_tile = b - a;
-  uint64_t* run = running + static_cast<size_t>(row) * K;
-  for (int i = threadIdx.x; i < n_run; i += NT) s_run[i] = run[i];
-  __syncthreads();
+  uint64_t* run = pool + static_cast<size_t>(row) * CAP;
   const float* lg = tile_logits + static_cast<size_t>(row) * tile + (a - lo);   // position a at lg[0]
-  auto src = [&](int64_t i, uint64_t& x) -> bool {
-    if (i < n_run) x = s_run[i];
-    else x = make_key(lg[i - n_run], static_cast<uint32_t>(a + (i - n_run)));
-    return true;
-  };
-  const int64_t n = static_cast<int64_t>(n_run) + n_tile;
-  if (n_run == K) {
-    // The running set is full: only tile keys above its smallest key can enter.
-    // One pass over the tile collects those into LDS; the select then runs over
-    // LDS only (unless too many enter, then the general path below).
-    if (threadIdx.x == 0) {
-      s_min = ~0ull;
-      s_m = 0;
+  auto key_at = [&](int i) -> uint64_t { return make_key(lg[i], static_cast<uint32_t>(a + i)); };
+  if (threadIdx.x == 0) {
+    s_m = 0;
+    s_n = 0;
+  }
+  __syncthreads();
+  // eight logits per thread in flight before any is tested (the atomic append
+  // would otherwise serialise the loads into one round trip per step)
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < n_tile; i0 += NT * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
+      v[u] = i < n_tile ? lg[i] : 0.0f;
     }
-    __syncthreads();
-    uint64_t mn = ~0ull;
-    for (int i = threadIdx.x; i < K; i += NT) mn = min(mn, s_run[i]);
-    atomicMin(&s_min, mn);
-    __syncthreads();
-    const uint64_t floor_key = s_min;
-    for (int i = threadIdx.x; i < n_tile; i += NT) {
-      const uint64_t x = make_key(lg[i], static_cast<uint32_t>(a + i));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT + static_cast<int>(threadIdx.x);
+      if (i >= n_tile) continue;
+      const uint64_t x = make_key(v[u], static_cast<uint32_t>(a + i));
       if (x > floor_key) {
         const int at = atomicAdd(&s_m, 1);
         if (at < kTileNewCap) s_new[at] = x;
       }
     }
-    __syncthreads();
-    const int m = s_m;
-    if (m == 0) return;   // nothing of this tile reaches the row's top K
-    if (m <= kTileNewCap) {
-      auto lsrc = [&](int64_t i, uint64_t& x) -> bool {
-        x = i < K ? s_run[i] : s_new[i - K];
-        return true;
-      };
-      bool ok = false;
-      const uint64_t T = block_radix_select<NT, 8>(lsrc, K + m, K, s_hist, s_red, &ok);
-      if (threadIdx.x == 0) s_n = 0;
-      __syncthreads();
-      if (ok) {
-        for (int i = threadIdx.x; i < K + m; i += NT) {
-          uint64_t x;
-          lsrc(i, x);
-          if (x >= T) {
-            const int at = atomicAdd(&s_n, 1);
-            if (at < K) run[at] = x;
-          }
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) run_count[row] = (ok && s_n == K) ? K : -1;
-      return;
-    }
   }
-  if (n <= K) {   // everything fits: append the tile's keys
-    for (int i = threadIdx.x; i < n_tile; i += NT) {
-      uint64_t x;
-      src(n_run + i, x);
-      run[n_run + i] = x;
+  __syncthreads();
+  const int m = s_m;   // tile keys above the floor (all counted, at most kTileNewCap kept)
+  if (m == 0) return;
+  const bool in_lds = m <= kTileNewCap;
+  if (c + m <= CAP) {   // room in the pool: append
+    if (in_lds) {
+      for (int i = threadIdx.x; i < m; i += NT) run[c + i] = s_new[i];
+    } else {
+      for (int i = threadIdx.x; i < n_tile; i += NT) {
+        const uint64_t x = key_at(i);
+        if (x > floor_key) run[c + atomicAdd(&s_n, 1)] = x;
+      }
     }
-    if (threadIdx.x == 0) run_count[row] = static_cast<int32_t>(n);
+    if (threadIdx.x == 0) run_count[row] = c + m;
     return;
   }
+  // compact: top K of the pool and the tile's keys above the floor
+  for (int i = threadIdx.x; i < c; i += NT) s_pool[i] = run[i];
+  __syncthreads();
+  auto src = [&](int64_t i, uint64_t& x) -> bool {
+    if (i < c) {
+      x = s_pool[i];
+      return true;
+    }
+    if (in_lds) {
+      x = s_new[i - c];
+      return true;
+    }
+    x = key_at(static_cast<int>(i - c));
+    return x > floor_key;
+  };
+  const int64_t n = static_cast<int64_t>(c) + (in_lds ? m : n_tile);
   bool ok = false;
   const uint64_t T = block_radix_select<NT, 8>(src, n, K, s_hist, s_red, &ok);
-  if (threadIdx.x == 0) s_n = 0;
-  __syncthreads();
   if (ok) {
     for (int64_t i = threadIdx.x; i < n; i += NT) {
       uint64_t x;
-      src(i, x);
-      if (x >= T) {
+      if (src(i, x) && x >= T) {
         const int at = atomicAdd(&s_n, 1);
         if (at < K) run[at] = x;
       }
     }
   }
   __syncthreads();
-  // keys are unique, so exactly K keys are >= T; anything else is a selector failure
-  if (threadIdx.x == 0) run_count[row] = (ok && s_n == K) ? K : -1;
+  if (threadIdx.x == 0) {
+    const bool good = ok && s_n == K;
+    run_count[row] = good ? K : -1;   // -1: the emit fails the row closed
+    run_floor[row] = good ? T : ~0ull;
+  }
 }
 
+// Per long row: the top K of its pool (exact select when it holds more), then
+// the ascending position order and the page map.
 template <int K>
 __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restrict__ row_state,
-                                                        const uint64_t* __restrict__ running,
+                                                        const uint64_t* __restrict__ pool,
                                                         const int32_t* __restrict__ run_count,
                                                         const int32_t* __restrict__ page_table, int64_t P_log,
                                                         int32_t* __restrict__ out_raw, int32_t* __restrict__ out_slot,
                                                         int32_t* __restrict__ out_count, float* __restrict__ out_score) {
   constexpr int NT = 256;
+  constexpr int CAP = tile_pool_cap(K);
+  __shared__ uint64_t s_pool[CAP];
   __shared__ uint64_t s_sel[K];
+  __shared__ uint32_t s_hist[256];
+  __shared__ BlockScratch<NT> s_red;
+  __shared__ int32_t s_n;
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
-  if (run_count[row] != K) {   // a long row visits more than K positions: anything else is a failure
+  const int c = run_count[row];
+  if (c < K || c > CAP) {   // a long row visits more than K positions: anything else is a failure
     fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
     return;
   }
-  const uint64_t* run = running + static_cast<size_t>(row) * K;
-  for (int i = threadIdx.x; i < K; i += NT) s_sel[i] = run[i];
+  const uint64_t* run = pool + static_cast<size_t>(row) * CAP;
+  for (int i = threadIdx.x; i < c; i += NT) s_pool[i] = run[i];
+  if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
+  bool ok = true;
+  uint64_t T = 0;
+  if (c > K) {
+    auto src = [&](int64_t i, uint64_t& x) -> bool {
+      x = s_pool[i];
+      return true;
+    };
+    T = block_radix_select<NT, 8>(src, c, K, s_hist, s_red, &ok);
+  }
+  if (ok) {
+    for (int i = threadIdx.x; i < c; i += NT) {
+      const uint64_t x = s_pool[i];
+      if (x >= T) {
+        const int at = atomicAdd(&s_n, 1);
+        if (at < K) s_sel[at] = x;
+      }
+    }
+  }
+  __syncthreads();
+  if (!ok || s_n != K) {
+    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
+    return;
+  }
   emit_row<K, NT>(s_sel, row, page_table, P_log, out_raw, out_slot, out_count, out_score);
 }
 
@@ -1250,22 +1288,25 @@ hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32
 }
 
 hipError_t launch_tiled(const PathArgs& p, const int32_t* row_state, int32_t splits, int32_t tile, float* tile_logits,
-                        uint64_t* running, int32_t* run_count, hipStream_t st) {
+                        uint64_t* running, int32_t* run_count, uint64_t* run_floor, hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
   const int64_t S = p.P_log * kPage;
   const dim3 sgrid(static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta), static_cast<unsigned>(splits));
   const dim3 rgrid(static_cast<unsigned>(p.Q));
   const ScanArgs a = scan_args(p, row_state, splits);
-  tile_reset_kernel<<<dim3(static_cast<unsigned>((p.Q + 255) / 256)), dim3(256), 0, st>>>(run_count, p.Q);
+  tile_reset_kernel<<<dim3(static_cast<unsigned>((p.Q + 255) / 256)), dim3(256), 0, st>>>(run_count, run_floor,
+                                                                                           p.Q);
   for (int64_t lo = 0; lo < S; lo += tile) {
     const int32_t hi = static_cast<int32_t>(lo + tile < S ? lo + tile : S);
     dense_score_kernel<<<sgrid, dim3(kCtaThreads), 0, st>>>(a, tile_logits, tile, static_cast<int32_t>(lo), hi);
     if (p.K == 512)
       tile_merge_kernel<512><<<rgrid, dim3(256), 0, st>>>(row_state, p.row_start, p.row_end, tile_logits, tile,
-                                                          static_cast<int32_t>(lo), hi, running, run_count);
+                                                          static_cast<int32_t>(lo), hi, running, run_count,
+                                                          run_floor);
     else
       tile_merge_kernel<1024><<<rgrid, dim3(256), 0, st>>>(row_state, p.row_start, p.row_end, tile_logits, tile,
-                                                           static_cast<int32_t>(lo), hi, running, run_count);
+                                                           static_cast<int32_t>(lo), hi, running, run_count,
+                                                           run_floor);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

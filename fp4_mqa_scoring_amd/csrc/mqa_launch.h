@@ -48,6 +48,10 @@ struct GatedScratch {
 // into the exact fallback.
 constexpr int candidate_cap(int K) { return K == 512 ? 3072 : 4096; }
 
+// Keys a row's pool holds in the context-tiled path (K after each compaction,
+// appended tile keys above its floor up to this many).
+constexpr int tile_pool_cap(int K) { return 2 * K; }
+
 // mode 0: TopK (answers short and invalid rows); mode 1: logits only.
 // fb_count (nullable) is cleared for the gated path.
 hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int32_t* fb_count, hipStream_t st);
@@ -82,7 +86,7 @@ hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t spli
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.
 hipError_t launch_tiled(const PathArgs& p, const int32_t* row_state, int32_t splits, int32_t tile, float* tile_logits,
-                        uint64_t* running, int32_t* run_count, hipStream_t st);
+                        uint64_t* running, int32_t* run_count, uint64_t* run_floor, hipStream_t st);
 hipError_t launch_logits_topk(const PathArgs& p, const float* logits, const int32_t* row_state,
                               hipStream_t st);
 // Copies the sticky status word to *host_out and clears it (synchronises st).

@@ -147,10 +147,11 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
  * context is visited in tiles of tile_positions logical positions (a multiple
  * of 256; 0 = 4096); per tile the fp32 scores of every row are written to a
  * [Q, tile_positions] scratch buffer by the dense scorer, and every long row
- * merges its running exact top-K with the tile's keys by exact radix select. No
+ * appends the tile's keys above its floor to a pool of at most 2K keys,
+ * compacted to its exact top K by radix select when full. No
  * gate, no calibration. Outputs are identical to mqa_fp4_topk_prefill's
  * (scores bit-identical). Stream-ordered scratch:
- * mqa_fp4_tiled_scratch_bytes(Q, K, tile) = O(Q) + Q*K*8 + Q*tile*4 bytes,
+ * mqa_fp4_tiled_scratch_bytes(Q, K, tile) = O(Q) + Q*2K*8 + Q*tile*4 bytes,
  * independent of the context length. Returns MQA_ERR_BAD_SIZE for a bad tile.
  */
 int32_t mqa_fp4_tiled_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,

@@ -123,9 +123,10 @@ def test_tiled_path_checks_tile_and_k_on_host(lib):
     assert lib.mqa_fp4_tiled_topk_prefill(*args, 512, 300, p, p, p, None, None) == -4     # not a multiple of 256
     assert lib.mqa_fp4_tiled_topk_prefill(*args, 512, -256, p, p, p, None, None) == -4
     assert lib.mqa_fp4_tiled_topk_prefill(*args, 640, 256, p, p, p, None, None) == -1     # unsupported K
-    # scratch: O(Q) + Q*K*8 + Q*tile*4, no context argument at all
+    # scratch: O(Q) + Q*2K*8 (the pool) + Q*tile*4, no context argument at all
     q, K, T = 1000, 1024, 4096
-    want = 2 * ((q * 4 + 255) // 256 * 256) + (q * K * 8 + 255) // 256 * 256 + (q * T * 4 + 255) // 256 * 256
+    a = lambda x: (x + 255) // 256 * 256
+    want = 2 * a(q * 4) + a(q * 8) + a(q * 2 * K * 8) + a(q * T * 4)
     assert m.mqa_fp4_tiled_scratch_bytes(q, K, T) == want
     assert m.mqa_fp4_tiled_scratch_bytes(q, K, 0) == want      # 0 = the 4096 default
 
