@@ -280,6 +280,14 @@ def bench_decode(args, torch, mqa, dev):
     n = d.lengths()
     ok = bool(np.all(counts == np.minimum(n, K)))
     key_bytes = pairs * DECODE_BYTES_PER_PAIR
+    # scaled FETCH_SIZE + WRITE_SIZE bytes of one gated-scan launch, if counted on these sources
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "decode_gscan_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == code_hash("mqa_device.h", "mqa_select.h", "mqa_decode.hip"):
+            traffic = tr.get("bytes_per_launch")
     line = {
         "metric": "ms/call + scored pairs/s, decode batch (multi-sequence form, HIP graph replay)",
         "value": pairs / (wall_ms * 1e-3), "unit": "scored pairs/s", "n_gpus": 1, "steps": args.steps,
@@ -288,7 +296,7 @@ def bench_decode(args, torch, mqa, dev):
         "config": {"workload": "decode: 64 sequences x 1 row, C4 context 32768..131072, K=1024",
                    "Q": Q, "K": K, "scored_pairs": pairs, "workspace_bytes": ws.numel()},
         "roofline": {"bound": "hbm", "achieved": key_bytes / (scan_ms * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": key_bytes / (scan_ms * 1e-3) / HBM_PEAK, "traffic": None,
+                     "unit": "GB/s", "frac": key_bytes / (scan_ms * 1e-3) / HBM_PEAK, "traffic": traffic,
                      "kernel": "decode_gscan_kernel<1024>", "kernel_ms": scan_ms,
                      "graph_replay_ms": graph_ms, "eager_call_ms": eager_ms,
                      "call_key_gbs": key_bytes / (graph_ms * 1e-3) / 1e9,
