@@ -740,16 +740,28 @@ __global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ 
     };
     bool ok = false;
     const uint64_t T = block_radix_select<NT, 8>(src, static_cast<int64_t>(n), K, s_hist, s_red, &ok);
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
     if (ok) {
-      for (int i = threadIdx.x; i < static_cast<int>(n); i += NT) {
+      // Stable gather: thread t takes the contiguous chunk [t C, t C + C) of the
+      // candidates, and a suffix count places it; the kept keys stay in buffer
+      // order. A row whose candidates came from one wave (one split) is then
+      // already in ascending position order and the emit skips its sort.
+      const int C = (static_cast<int>(n) + NT - 1) / NT;
+      const int i0 = min(static_cast<int>(n), static_cast<int>(threadIdx.x) * C);
+      const int i1 = min(static_cast<int>(n), i0 + C);
+      uint32_t cnt = 0;
+      for (int i = i0; i < i1; ++i) cnt += keys[i] >= T ? 1u : 0u;
+      const uint32_t incl = block_suffix_sum<NT>(cnt, s_red);   // kept keys in chunks t .. NT-1
+      int at = K - static_cast<int>(incl);
+      for (int i = i0; i < i1; ++i) {
         const uint64_t x = keys[i];
         if (x >= T) {
-          const int at = atomicAdd(&s_n, 1);
-          if (at < K) s_sel[at] = x;
+          if (at >= 0 && at < K) s_sel[at] = x;
+          ++at;
         }
       }
+      if (threadIdx.x == 0) s_n = static_cast<int>(incl);   // all kept keys
+    } else if (threadIdx.x == 0) {
+      s_n = 0;
     }
     __syncthreads();
     if (!ok || s_n != K) {

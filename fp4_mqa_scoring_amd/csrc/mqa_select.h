@@ -264,10 +264,16 @@ __device__ __forceinline__ void emit_row(uint64_t* s_sel, int64_t row, const int
     s_sel[i] = (static_cast<uint64_t>(key_pos(key)) << 32) | static_cast<uint32_t>(key >> 32);
   }
   __syncthreads();
-  if constexpr (K <= NT)
-    block_sort_regs<K, NT>(s_sel);
-  else
-    block_bitonic_sort<K, NT>(s_sel);
+  // keys gathered in buffer order from one wave's appends are already in
+  // ascending position order: one compare per element instead of the sort
+  int unsorted = 0;
+  for (int i = threadIdx.x; i + 1 < K; i += NT) unsorted |= s_sel[i] > s_sel[i + 1];
+  if (__syncthreads_or(unsorted)) {
+    if constexpr (K <= NT)
+      block_sort_regs<K, NT>(s_sel);
+    else
+      block_bitonic_sort<K, NT>(s_sel);
+  }
   const size_t base = static_cast<size_t>(row) * K;
   for (int i = threadIdx.x; i < K; i += NT) {
     const uint64_t v = s_sel[i];
