@@ -75,7 +75,6 @@ __device__ __forceinline__ uint64_t window_lanes(int p0, int start, int end) {
 // ---------------------------------------------------------------------------
 // Wave helpers (wave64).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ int mbcnt64(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),

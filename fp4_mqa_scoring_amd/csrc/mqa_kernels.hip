@@ -98,8 +98,6 @@ __global__ void __launch_bounds__(256) row_prep_kernel(
   }
 }
 
-// Physical page of a page-table entry, or -1 when it is out of range.
-__device__ __forceinline__ int64_t page_or_neg(int32_t e, int64_t P_phys) { return (e >= 0 && e < P_phys) ? e : -1; }
 
 struct ScanArgs {
   const uint8_t* q;
