@@ -426,7 +426,9 @@ def test_logits_selector_total_order_on_special_value_arrays(S, lo, hi):
 
 # --- the benchmark workloads at full size, sampled rows -------------------------------------
 
-@pytest.mark.parametrize("cfg,nrows", [(2, 6), (3, 4), (4, 4), (5, 4)])
+# 256 sampled rows (4x the 64 that the long prefills' workload definitions name)
+# for the two long prefills and the headline shape, 64 for the Q=1024 grids
+@pytest.mark.parametrize("cfg,nrows", [(2, 64), (3, 64), (4, 256), (5, 256), ("H", 256)])
 def test_full_size_workloads_sampled_rows(cfg, nrows):
     _need_gpu()
     inp = synth.make_config(cfg)
@@ -445,5 +447,5 @@ def test_full_size_workloads_sampled_rows(cfg, nrows):
         st = int(inp.row_start[r])
         assert np.array_equal(raw[r], np.arange(st, st + inp.K)), r
         assert np.all(score[r] == 0)
-    rows = synth.sample_rows(inp, nrows, seed=cfg)
+    rows = synth.sample_rows(inp, nrows, seed=synth.config_seed(cfg))
     check_rows(inp, rows, raw, slot, cnt, score, where=f"config {cfg}")
