@@ -151,6 +151,15 @@ constexpr int kCalStride = 32;
 constexpr int kCalPerPage = kPage / kCalStride;   // sampled positions per page
 static_assert(kCalStride >= 16 && kCalStride <= kPage && kPage % kCalStride == 0, "stride divides the page");
 constexpr int kCalCap = 512;         // calibration pool per row
+// Context splits of the calibration (rows with few row tiles): each split keeps
+// the exact top-k' of its sample blocks in a list of at most kCalListCap keys in
+// the row's candidate buffer (unused until the scan), followed by one header
+// word per split; a combine kernel takes the k'-th key of the lists' union.
+constexpr int kCalMaxSplits = 8;
+constexpr int kCalMinSplitBlocks = 6;   // fewer sample blocks per split: the combine launch costs more than it saves
+constexpr int kCalListCap = 128;
+constexpr int kCalHeaders = kCalMaxSplits * kCalListCap;   // header words start here
+static_assert(kCalHeaders + kCalMaxSplits <= 3072, "split lists fit the smallest candidate buffer");
 
 // Score blocks [a, a+n) visited by a CTA.
 struct BlockSeq {
@@ -480,7 +489,8 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
     SampleDma d;
     d.init(u0, wave, lane);
     const LaneOffsets lo = lane_offsets(lane);
-    const BlockSeq seq{0, (u1 - u0 + kCalStride - 1) / kCalStride};
+    const BlockSeq seq = split_range(0, (u1 - u0 + kCalStride - 1) / kCalStride, static_cast<int>(blockIdx.y),
+                                     static_cast<int>(gridDim.y));
     stream_dma(a, d, seq, s_codes0, s_scales0, s_codes1, s_scales1,
                [&](int v, const uint8_t* codes, const uint8_t* scales) {
       if (!gated) return;
@@ -509,6 +519,27 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
   }
   if (!active) return;
   wave_lds_sync();
+  if (gridDim.y > 1) {
+    // split: this split's exact top-min(k', fill) keys and a header word
+    // (bit 63 selector failure, bit 62 gated, bits 32..47 k', bits 0..31 keys)
+    uint64_t* list = c.cand + static_cast<size_t>(row) * c.cap;
+    int n = 0;
+    if (gated) {
+      if (fill > kp) {
+        const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
+        if (sel.kept != kp) bad = true;
+        fill = kp;
+      }
+      if (kp > kCalListCap) bad = true;
+      n = bad ? 0 : fill;
+      uint64_t* dst = list + static_cast<size_t>(blockIdx.y) * kCalListCap;
+      for (int i = lane; i < n; i += 64) dst[i] = pool[i];
+    }
+    if (lane == 0)
+      list[kCalHeaders + blockIdx.y] = (bad ? 1ull << 63 : 0ull) | (gated ? 1ull << 62 : 0ull) |
+                                       (static_cast<uint64_t>(kp & 0xFFFF) << 32) | static_cast<uint32_t>(n);
+    return;
+  }
   uint32_t start_count = 0;
   uint64_t row_gate = 0;
   if (mode == 1) {
@@ -524,6 +555,55 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
       T = sel.T;
     } else {
       T = wave_min_key(pool, fill, lane);
+    }
+    row_gate = T - 1;
+    if (bad) {                                        // selector failure: exact fallback
+      start_count = static_cast<uint32_t>(c.cap) + 1;
+      row_gate = ~0ull;
+    }
+  }
+  if (lane == 0) {
+    c.count[row] = start_count;
+    c.gate[row] = row_gate;
+  }
+}
+
+// Combine of a split calibration (mode 0 only): per long row, the k'-th key of
+// the union of the splits' top-k' lists is the k'-th key of the whole sample,
+// so the gate equals the one an unsplit calibration sets.
+constexpr int kCombineRows = 4;
+__global__ void __launch_bounds__(64 * kCombineRows) calib_combine_kernel(ScanArgs a, CandArgs c, int splits) {
+  __shared__ uint64_t s_pool[kCombineRows][kCalMaxSplits * kCalListCap];
+  __shared__ uint32_t s_hist[kCombineRows][256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kCombineRows + wave;
+  if (row >= a.Q || a.row_state[row] != kRowLong) return;
+  const uint64_t* list = c.cand + static_cast<size_t>(row) * c.cap;
+  uint64_t* pool = s_pool[wave];
+  bool bad = false, gated = false;
+  int kp = 0, n = 0;
+  for (int s = 0; s < splits; ++s) {
+    const uint64_t h = list[kCalHeaders + s];
+    bad |= (h >> 63) != 0;
+    gated = ((h >> 62) & 1ull) != 0;
+    kp = static_cast<int>((h >> 32) & 0xFFFF);
+    const int ns = static_cast<int>(static_cast<uint32_t>(h));
+    for (int i = lane; i < ns; i += 64) pool[n + i] = list[static_cast<size_t>(s) * kCalListCap + i];
+    n += ns;
+  }
+  uint32_t start_count = 0;
+  uint64_t row_gate = 0;
+  if (gated) {
+    wave_lds_sync();
+    uint64_t T = 0;
+    if (!bad && n > kp) {
+      const Selected sel = wave_select_compact(pool, n, kp, s_hist[wave], lane);
+      if (sel.kept != kp) bad = true;
+      T = sel.T;
+    } else if (!bad && n == kp && n > 0) {
+      T = wave_min_key(pool, n, lane);
+    } else {
+      bad = true;
     }
     row_gate = T - 1;
     if (bad) {                                        // selector failure: exact fallback
@@ -1259,9 +1339,20 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
   const CandArgs c = cand_args(g, K);
   const unsigned tiles = static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta);
   switch (stage) {
-    case 0:
-      calib_kernel<K><<<dim3(tiles), dim3(kCtaThreads), 0, st>>>(a, c, calib_mode);
+    case 0: {
+      // split the calibration over the context when the row tiles alone leave CUs
+      // idle and every split still gets kCalMinSplitBlocks sample blocks
+      const int64_t sample_blocks = (p.P_log * kPage + kCalStride * kTile - 1) / (kCalStride * kTile);
+      int64_t cs = calib_mode == 0 ? splits : 1;
+      if (cs > kCalMaxSplits) cs = kCalMaxSplits;
+      if (cs > sample_blocks / kCalMinSplitBlocks) cs = sample_blocks / kCalMinSplitBlocks;
+      if (cs < 1) cs = 1;
+      calib_kernel<K><<<dim3(tiles, static_cast<unsigned>(cs)), dim3(kCtaThreads), 0, st>>>(a, c, calib_mode);
+      if (cs > 1)
+        calib_combine_kernel<<<dim3(static_cast<unsigned>((p.Q + kCombineRows - 1) / kCombineRows)),
+                               dim3(64 * kCombineRows), 0, st>>>(a, c, static_cast<int>(cs));
       break;
+    }
     case 1:
       scan_kernel<K><<<dim3(tiles, static_cast<unsigned>(splits)), dim3(kCtaThreads), 0, st>>>(a, c);
       break;

@@ -145,6 +145,32 @@ def test_splits_do_not_change_outputs(K):
 
 
 @pytest.mark.parametrize("K", [512, 1024])
+def test_split_calibration_gives_identical_outputs(K):
+    """On a long context the calibration is split over the context as the scan is
+    (2, 4 and 8 splits here); the union of the splits' exact top-k' lists has the
+    sample's k'-th key, so the gate, and every output bit, equals the unsplit
+    run's."""
+    _need_gpu()
+    Q, S = 16, 393216
+    rng = np.random.default_rng(300 + K)
+    en = (S - rng.integers(0, 4000, Q)).astype(np.int32)
+    st = np.zeros(Q, np.int32)
+    st[1], en[1] = 70000, 70000 + 40000              # a window inside the context
+    st[2], en[2] = 5, S                               # unaligned start
+    st[3], en[3] = 1000, 1000 + K + 300               # a short long-row (sample of ~50)
+    st[4], en[4] = 9, 9 + K                           # exactly K: short
+    inp = synth.make_inputs(Q, S, K, 5150 + K, row_start=st, row_end=en, P_phys=S // 64 + 2)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K, flags=1)
+    check_rows(inp, range(Q), *base, where=f"split calibration K={K}")
+    for splits in (2, 4, 8, 17, 0):
+        got = gu.run_fused(dev, K, flags=splits)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"splits={splits}"
+    assert mqa.mqa_fp4_status() == 0
+
+
+@pytest.mark.parametrize("K", [512, 1024])
 def test_prefilter_off_and_forced_underfill_give_identical_outputs(K):
     """The calibrated gate is a pure speed-up: without it (every long row on the
     exact ungated path) and with a gate above every key (every long row
