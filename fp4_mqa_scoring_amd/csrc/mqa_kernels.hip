@@ -447,7 +447,9 @@ __device__ __forceinline__ uint64_t wave_min_key(const uint64_t* pool, int n, in
 // underfilled row is still exact, it just takes the fallback. Rows whose sample
 // is not larger than k' get no gate. mode 1 sends every long row to the exact
 // fallback (no prefilter), mode 2 forces an underfill (gate above every key);
-// both exist for testing.
+// both exist for testing. With gridDim.y > 1 (mode 0 only) split y streams its
+// share of the sample blocks and leaves its exact top-k' list and a header word
+// in the row's candidate buffer for calib_combine_kernel, which sets the gate.
 // ---------------------------------------------------------------------------
 template <int K>
 __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandArgs c, int mode) {
