@@ -71,7 +71,7 @@ extern "C" {
 #define MQA_ERR_UNSUPPORTED_K (-1)   /* K not in {512, 1024} (PR 5309: explicit supported-K contract) */
 #define MQA_ERR_NULL_POINTER (-2)    /* a required pointer is NULL while its tensor is non-empty */
 #define MQA_ERR_MISALIGNED (-3)      /* a pointer breaks the alignment stated above */
-#define MQA_ERR_BAD_SIZE (-4)        /* negative size, or 64*P_log / 64*P_phys / Q*K beyond int32 */
+#define MQA_ERR_BAD_SIZE (-4)        /* negative size, or Q / 64*P_log / 64*P_phys beyond int32 */
 #define MQA_ERR_DEVICE (-5)          /* not device memory, tensors on different devices, stream on
                                         another device, or the device is not gfx950 */
 #define MQA_ERR_CAPTURING (-6)       /* the stream is capturing a graph */
@@ -99,9 +99,9 @@ extern "C" {
 
 /*
  * Fused FP4 scoring + exact TopK + page mapping (the hot path).
- *   num_rows          Q >= 0
+ *   num_rows          0 <= Q <= INT32_MAX
  *   num_phys_pages    P_phys >= 0, 64 * P_phys <= INT32_MAX
- *   num_logical_pages P_log >= 0, 64 * P_log <= INT32_MAX
+ *   num_logical_pages P_log >= 0, 64 * P_log <= INT32_MAX - 512
  *   K                 512 or 1024
  * Returns MQA_OK or a negative MQA_ERR_*.
  */
@@ -214,7 +214,8 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
  * streaming TopK", Changes and Scope; decode is the adjacent shape that
  * "[AMD][DSv4] Add experimental AITER FP4 streaming TopK" keeps on the older
  * path, and graph capture the support PR 5282's Scope defers).
- *   block_table int32 [num_seqs, max_pages]   64 * max_pages <= INT32_MAX
+ *   block_table int32 [num_seqs, max_pages]   64 * max_pages <= INT32_MAX - 512,
+ *                                             num_seqs * max_pages <= INT32_MAX
  *   seq_of_row  int32 [Q]                     a row whose sequence is outside
  *                                             [0, num_seqs) fails with code -1
  *   workspace   device memory of at least mqa_fp4_decode_workspace_bytes(Q, K,
