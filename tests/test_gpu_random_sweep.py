@@ -5,7 +5,10 @@ negated weights and rows with all-equal scores. Every entry point that returns
 a TopK runs on it: the fused path with random flags and splits, the context-
 tiled path with a random tile, and the decode form with one sequence. Every row
 of each is checked against the oracle, and the three agree bit for bit on raw
-indices, slots and counts. Failure messages name the case's seed and shape."""
+indices, slots and counts. A second set draws a few rows over long contexts
+(65K-397K positions) and random context splits, so that the calibration runs
+split and the merges see several splits' candidates. Failure messages name the
+case's seed and shape."""
 import numpy as np
 import pytest
 
@@ -17,6 +20,7 @@ from test_gpu_parity import check_rows
 pytestmark = pytest.mark.gpu
 
 N_CASES = 24
+N_LONG_CASES = 12
 
 
 def draw_case(seed):
@@ -57,6 +61,36 @@ def draw_case(seed):
     return inp, flags, tile
 
 
+def draw_long_case(seed):
+    """A few rows over a long context (65,536 .. 396,736 positions): the
+    calibration runs split over the context when splits > 1."""
+    rng = np.random.Generator(np.random.PCG64(10_000 + seed))
+    K = int(rng.choice([512, 1024]))
+    S = 64 * int(rng.integers(1024, 6200))
+    Q = int(rng.integers(1, 20))
+    start = np.zeros(Q, np.int64)
+    end = np.zeros(Q, np.int64)
+    for r in range(Q):
+        kind = int(rng.integers(0, 5))
+        if kind == 0:                                     # short
+            n = int(rng.integers(1, K + 1))
+            start[r] = int(rng.integers(0, S - n + 1))
+            end[r] = start[r] + n
+        elif kind == 1:                                   # causal-like: almost the whole context
+            end[r] = S - int(rng.integers(0, 3000))
+        elif kind == 2:                                   # a little longer than K
+            n = int(rng.integers(K + 1, 4 * K))
+            start[r] = int(rng.integers(0, S - n + 1))
+            end[r] = start[r] + n
+        else:                                             # any window
+            a, b = sorted(int(x) for x in rng.integers(0, S + 1, 2))
+            start[r], end[r] = a, b
+    inp = synth.make_inputs(Q, S, K, 70_000 + seed, row_start=start, row_end=end, P_phys=S // 64 + 2,
+                            tie_rows=int(rng.integers(0, 2)) if Q > 1 else 0,
+                            name=f"long sweep seed {seed}: Q={Q} S={S} K={K}")
+    return inp, int(rng.integers(2, 18))
+
+
 def run_decode_one_sequence(dev, K):
     import torch
     Q = dev["q"].shape[0]
@@ -90,3 +124,24 @@ def test_random_case(seed):
         for i, what in enumerate(("raw", "slot", "count")):
             assert np.array_equal(fused[i], other[i]), f"{tag}: fused and {name} differ in {what}"
     mqa.mqa_fp4_status()   # clear the sticky bits that fail-closed rows set
+
+
+@pytest.mark.parametrize("seed", range(N_LONG_CASES))
+def test_random_long_case(seed):
+    """One context split against several (calibration split too), every row
+    against the oracle, and the decode form bit-equal to both."""
+    if not gu.has_gpu():
+        pytest.skip("no GPU")
+    inp, splits = draw_long_case(seed)
+    dev = gu.to_device(inp)
+    tag = f"{inp.name} splits={splits}"
+    print(tag, flush=True)
+    base = gu.run_fused(dev, inp.K, flags=1)
+    check_rows(inp, range(inp.Q), *base, where=f"{tag} one split")
+    got = gu.run_fused(dev, inp.K, flags=splits)
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag}: splits change the outputs"
+    dec = run_decode_one_sequence(dev, inp.K)
+    for i, what in enumerate(("raw", "slot", "count")):
+        assert np.array_equal(base[i], dec[i]), f"{tag}: fused and decode differ in {what}"
+    mqa.mqa_fp4_status()
