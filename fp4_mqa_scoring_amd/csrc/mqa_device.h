@@ -266,10 +266,15 @@ __device__ __forceinline__ GroupAcc mfma_group(const QRow& r, const uint8_t* s_c
   const int ks = *reinterpret_cast<const uint16_t*>(s_scales + o.scale + GRP * 32 * kVecScales);
   const v16f z = {};
   GroupAcc acc;
+  // the wave issues its group's four MFMAs at raised priority, so the SIMD's
+  // arbiter keeps them together rather than interleaving other waves' epilogue
+  // instructions between them (measured: scan kernel about 1% shorter)
+  __builtin_amdgcn_s_setprio(1);
   acc.d0 = mfma_fp4<0, 0>(r.a[0][0], b0, z, r.scale, ks);
   acc.d0 = mfma_fp4<1, 1>(r.a[0][1], b1, acc.d0, r.scale, ks);
   acc.d1 = mfma_fp4<2, 0>(r.a[1][0], b0, z, r.scale, ks);
   acc.d1 = mfma_fp4<3, 1>(r.a[1][1], b1, acc.d1, r.scale, ks);
+  __builtin_amdgcn_s_setprio(0);
   return acc;
 }
 
