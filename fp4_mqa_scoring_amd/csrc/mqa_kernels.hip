@@ -4,7 +4,9 @@
 //   row_prep     validate windows and pages, answer short rows (length <= K)
 //   calib        per row: score a sample (every 32nd position of the row tile's
 //                range), keep the sample's exact top-k' and derive the gate T0 =
-//                its k'-th key
+//                its k'-th key (split over the context when the row tiles alone
+//                leave CUs idle; calib_combine then takes the k'-th key of the
+//                splits' lists)
 //   scan         per (8-row tile, context split): score every 256-position block
 //                with MXFP4 MFMA, ReLU + head-weighted sum in registers; keys >= T0
 //                are staged per wave in LDS and appended to the row's bounded
