@@ -5,7 +5,7 @@ negated weights and rows with all-equal scores. Every entry point that returns
 a TopK runs on it: the fused path with random flags and splits, the context-
 tiled path with a random tile, and the decode form with one sequence. Every row
 of each is checked against the oracle, and the three agree bit for bit on raw
-indices, slots and counts. A second set draws a few rows over long contexts
+indices, slots, counts and scores. A second set draws a few rows over long contexts
 (65K-397K positions) and random context splits, so that the calibration runs
 split and the merges see several splits' candidates. Failure messages name the
 case's seed and shape."""
@@ -121,8 +121,9 @@ def test_random_case(seed):
     dec = run_decode_one_sequence(dev, inp.K)
     check_rows(inp, range(inp.Q), *dec, where=f"{tag} decode")
     for name, other in (("tiled", tiled), ("decode", dec)):
-        for i, what in enumerate(("raw", "slot", "count")):
-            assert np.array_equal(fused[i], other[i]), f"{tag}: fused and {name} differ in {what}"
+        for i, what in enumerate(("raw", "slot", "count", "score")):
+            assert np.array_equal(np.asarray(fused[i]).view(np.uint32), np.asarray(other[i]).view(np.uint32)), \
+                f"{tag}: fused and {name} differ in {what}"
     mqa.mqa_fp4_status()   # clear the sticky bits that fail-closed rows set
 
 
@@ -142,6 +143,7 @@ def test_random_long_case(seed):
     for a, b in zip(base, got):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag}: splits change the outputs"
     dec = run_decode_one_sequence(dev, inp.K)
-    for i, what in enumerate(("raw", "slot", "count")):
-        assert np.array_equal(base[i], dec[i]), f"{tag}: fused and decode differ in {what}"
+    for i, what in enumerate(("raw", "slot", "count", "score")):
+        assert np.array_equal(np.asarray(base[i]).view(np.uint32), np.asarray(dec[i]).view(np.uint32)), \
+            f"{tag}: fused and decode differ in {what}"
     mqa.mqa_fp4_status()
