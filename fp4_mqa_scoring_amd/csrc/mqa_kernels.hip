@@ -158,7 +158,7 @@ constexpr int kCalCap = 512;         // calibration pool per row
 // the row's candidate buffer (unused until the scan), followed by one header
 // word per split; a combine kernel takes the k'-th key of the lists' union.
 constexpr int kCalMaxSplits = 8;
-constexpr int kCalMinSplitBlocks = 6;   // fewer sample blocks per split: the combine launch costs more than it saves
+constexpr int kCalMinSplitBlocks = 4;   // fewer sample blocks per split: the combine launch costs more than it saves
 constexpr int kCalListCap = 128;
 constexpr int kCalHeaders = kCalMaxSplits * kCalListCap;   // header words start here
 static_assert(kCalHeaders + kCalMaxSplits <= 3072, "split lists fit the smallest candidate buffer");
