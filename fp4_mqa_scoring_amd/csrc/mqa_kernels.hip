@@ -816,28 +816,35 @@ __global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ 
     for (int i = threadIdx.x; i < K; i += NT) s_sel[i] = keys[i];
     __syncthreads();
   } else {
-    auto src = [&](int64_t i, uint64_t& x) -> bool {
-      x = keys[i];
-      return true;
-    };
+    // Thread t holds the contiguous chunk [t C, t C + C) of the candidates in
+    // registers (C <= E: n <= cap) for the radix passes and the gather.
+    constexpr int E = (candidate_cap(K) + NT - 1) / NT;
+    const int C = (static_cast<int>(n) + NT - 1) / NT;
+    const int i0 = min(static_cast<int>(n), static_cast<int>(threadIdx.x) * C);
+    const int m = min(static_cast<int>(n), i0 + C) - i0;   // keys in this thread's chunk
+    uint64_t x[E];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      x[j] = j < m ? keys[i0 + j] : 0ull;
+      if (j < m) valid |= 1u << j;
+    }
     bool ok = false;
-    const uint64_t T = block_radix_select<NT, 8>(src, static_cast<int64_t>(n), K, s_hist, s_red, &ok);
+    const uint64_t T = block_radix_select_regs<NT, 8, E>(x, valid, K, s_hist, s_red, &ok);
     if (ok) {
-      // Stable gather: thread t takes the contiguous chunk [t C, t C + C) of the
-      // candidates, and a suffix count places it; the kept keys stay in buffer
-      // order. A row whose candidates came from one wave (one split) is then
-      // already in ascending position order and the emit skips its sort.
-      const int C = (static_cast<int>(n) + NT - 1) / NT;
-      const int i0 = min(static_cast<int>(n), static_cast<int>(threadIdx.x) * C);
-      const int i1 = min(static_cast<int>(n), i0 + C);
+      // Stable gather: a suffix count over the chunks places thread t's kept
+      // keys; they stay in buffer order. A row whose candidates came from one
+      // wave (one split) is then already in ascending position order and the
+      // emit skips its sort.
       uint32_t cnt = 0;
-      for (int i = i0; i < i1; ++i) cnt += keys[i] >= T ? 1u : 0u;
+#pragma unroll
+      for (int j = 0; j < E; ++j) cnt += (((valid >> j) & 1u) && x[j] >= T) ? 1u : 0u;
       const uint32_t incl = block_suffix_sum<NT>(cnt, s_red);   // kept keys in chunks t .. NT-1
       int at = K - static_cast<int>(incl);
-      for (int i = i0; i < i1; ++i) {
-        const uint64_t x = keys[i];
-        if (x >= T) {
-          if (at >= 0 && at < K) s_sel[at] = x;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        if (((valid >> j) & 1u) && x[j] >= T) {
+          if (at >= 0 && at < K) s_sel[at] = x[j];
           ++at;
         }
       }
