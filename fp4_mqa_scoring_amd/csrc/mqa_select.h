@@ -194,61 +194,69 @@ __device__ __forceinline__ void gather_at_least(const uint64_t (&x)[E], uint32_t
   }
 }
 
-// Sorts N (power of two) 64-bit values ascending in LDS with NT threads: the
-// bitonic network one compare-exchange per thread pair and barrier per stage.
-template <int N, int NT>
-__device__ __forceinline__ void block_bitonic_sort(uint64_t* v) {
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < N / 2; i += NT) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const uint64_t x = v[lo], y = v[hi];
-        if ((x > y) == up) {
-          v[lo] = y;
-          v[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
+// Sorts the K values v[] (LDS) ascending by their high 32 bits, which are
+// distinct non-negative positions: K position buckets between the smallest and
+// largest position (a monotone bucket function, so bucket order is position
+// order), a prefix sum of the bucket counts, a scatter into the buckets, and
+// inside each bucket a rank by counting the smaller positions: about ten
+// barriers where a bitonic network takes fifty-five (K = 1024).
+template <int K, int NT>
+__device__ __forceinline__ void block_position_sort(uint64_t* v) {
+  __shared__ uint64_t s_tmp[K];
+  __shared__ uint32_t s_start[K];
+  __shared__ uint32_t s_fill[K];
+  __shared__ BlockScratch<NT> s;
+  const int tid = threadIdx.x;
+  int hi = INT_MIN, nlo = INT_MIN;
+  for (int i = tid; i < K; i += NT) {
+    const int p = static_cast<int>(v[i] >> 32);
+    hi = max(hi, p);
+    nlo = max(nlo, -p);
   }
-}
-
-// The same network with one value per thread (64 <= N <= NT): thread t < N holds
-// element t in a register; a stride < 64 pairs lanes of one wave (shuffle, no
-// barrier) and only strides >= 64 go through LDS (10 of the 55 stages at
-// N = 1024). Threads t >= N only join the barriers. Measured faster than the
-// LDS network when N <= NT; with several values per thread (256 threads,
-// N = 1024) the shuffles cost more LDS instructions than they save.
-template <int N, int NT>
-__device__ __forceinline__ void block_sort_regs(uint64_t* v) {
-  static_assert(N >= 64 && N <= NT && (N & (N - 1)) == 0, "one value per thread");
-  const int t = threadIdx.x;
-  const bool act = t < N;   // uniform per wave
-  uint64_t x = act ? v[t] : 0ull;
-  // element t keeps the smaller value iff (t is the lower index) == (its run ascends)
-  auto keep = [](uint64_t a, uint64_t b, bool lower, bool up) -> uint64_t {
-    return (lower == up) ? (a < b ? a : b) : (a < b ? b : a);
+  hi = block_max_i32<NT>(hi, s);
+  const int lo = -block_max_i32<NT>(nlo, s);
+  const float scale = static_cast<float>(K) / (static_cast<float>(hi - lo) + 1.0f);
+  auto bucket = [&](uint64_t x) -> int {
+    return min(K - 1, static_cast<int>(static_cast<float>(static_cast<int>(x >> 32) - lo) * scale));
   };
-#pragma unroll
-  for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 64) {
-        __syncthreads();   // earlier reads of v are done
-        if (act) v[t] = x;
-        __syncthreads();
-        if (act) x = keep(x, v[t ^ stride], (t & stride) == 0, (t & size) == 0);
-      } else if (act) {
-        const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), stride, 64);
-        const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), stride, 64);
-        x = keep(x, (static_cast<uint64_t>(hi) << 32) | lo, (t & stride) == 0, (t & size) == 0);
-      }
-    }
+  for (int b = tid; b < K; b += NT) {
+    s_start[b] = 0u;
+    s_fill[b] = 0u;
   }
   __syncthreads();
-  if (act) v[t] = x;
+  for (int i = tid; i < K; i += NT) atomicAdd(&s_start[bucket(v[i])], 1u);
+  __syncthreads();
+  constexpr int B = (K + NT - 1) / NT;   // buckets per thread: [tid B, tid B + B)
+  uint32_t c[B];
+  uint32_t tsum = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int b = tid * B + j;
+    c[j] = b < K ? s_start[b] : 0u;
+    tsum += c[j];
+  }
+  uint32_t run = static_cast<uint32_t>(K) - block_suffix_sum<NT>(tsum, s);   // keys in earlier buckets
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const int b = tid * B + j;
+    if (b < K) s_start[b] = run;
+    run += c[j];
+  }
+  __syncthreads();
+  for (int i = tid; i < K; i += NT) {
+    const uint64_t x = v[i];
+    const int b = bucket(x);
+    s_tmp[s_start[b] + atomicAdd(&s_fill[b], 1u)] = x;
+  }
+  __syncthreads();
+  for (int k = tid; k < K; k += NT) {
+    const uint64_t x = s_tmp[k];
+    const int b = bucket(x);
+    const uint32_t s0 = s_start[b], n = s_fill[b], p = static_cast<uint32_t>(x >> 32);
+    uint32_t r = 0;
+    for (uint32_t j = s0; j < s0 + n; ++j) r += static_cast<uint32_t>(s_tmp[j] >> 32) < p ? 1u : 0u;
+    v[s0 + r] = x;
+  }
   __syncthreads();
 }
 
@@ -268,12 +276,7 @@ __device__ __forceinline__ void emit_row(uint64_t* s_sel, int64_t row, const int
   // ascending position order: one compare per element instead of the sort
   int unsorted = 0;
   for (int i = threadIdx.x; i + 1 < K; i += NT) unsorted |= s_sel[i] > s_sel[i + 1];
-  if (__syncthreads_or(unsorted)) {
-    if constexpr (K <= NT)
-      block_sort_regs<K, NT>(s_sel);
-    else
-      block_bitonic_sort<K, NT>(s_sel);
-  }
+  if (__syncthreads_or(unsorted)) block_position_sort<K, NT>(s_sel);
   const size_t base = static_cast<size_t>(row) * K;
   for (int i = threadIdx.x; i < K; i += NT) {
     const uint64_t v = s_sel[i];
