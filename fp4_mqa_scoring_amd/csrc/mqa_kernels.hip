@@ -133,12 +133,14 @@ struct Geometry;
 template <>
 struct Geometry<512> {
   static constexpr int kCap = candidate_cap(512);
-  static constexpr int kFbSplits = 4;
+  static constexpr int kFbSplits = 4;      // fallback splits per listed row: at most
+  static constexpr int kFbSplitsMin = 4;   // ... and when the list is long
 };
 template <>
 struct Geometry<1024> {
   static constexpr int kCap = candidate_cap(1024);
-  static constexpr int kFbSplits = 2;
+  static constexpr int kFbSplits = 4;
+  static constexpr int kFbSplitsMin = 2;
 };
 // Fallback pool per row: all LDS left after the block buffers and histograms.
 constexpr int kPoolCap = 1856;
@@ -713,8 +715,16 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
 // radix-selects the K largest, drops the rest and raises the gate. Per (row,
 // fallback split) the top-K keys go to the row's candidate buffer at split * K.
 // Persistent: a fixed grid loops over (8-row chunk of the list, split) items.
+// A short list takes FBS splits per row (more of the grid on each row: a lone
+// fallback row is what adds latency to a call); a long one FBS_MIN, which is
+// less merge work for the same scan work.
 // ---------------------------------------------------------------------------
-template <int K, int CAP, int FBS>
+__device__ __forceinline__ int fallback_splits(int listed, int fbs, int fbs_min) {
+  const int chunks = (listed + kRowsPerCta - 1) / kRowsPerCta;
+  return chunks * fbs <= kFallbackGrid ? fbs : fbs_min;
+}
+
+template <int K, int CAP, int FBS, int FBS_MIN>
 __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs a, CandArgs c) {
   static_assert(CAP >= K + 64, "pool must hold K keys plus one batch");
   MQA_BLOCK_BUFFERS;
@@ -725,8 +735,9 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int listed = *c.fb_count;
   const int chunks = (listed + kRowsPerCta - 1) / kRowsPerCta;
-  for (int item = blockIdx.x; item < chunks * FBS; item += gridDim.x) {
-    const int chunk = item / FBS, split = item % FBS;
+  const int fbs = fallback_splits(listed, FBS, FBS_MIN);
+  for (int item = blockIdx.x; item < chunks * fbs; item += gridDim.x) {
+    const int chunk = item / fbs, split = item % fbs;
     const int li = chunk * kRowsPerCta + wave;
     const bool active = li < listed;
     const int row = active ? c.fb_list[li] : 0;
@@ -737,7 +748,7 @@ __global__ void __launch_bounds__(kCtaThreads, 1) fallback_scan_kernel(ScanArgs 
     }
     int u0 = 0, u1 = 0;
     if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) continue;
-    const BlockSeq seq = split_range(u0, u1, split, FBS);
+    const BlockSeq seq = split_range(u0, u1, split, fbs);
     QRow qr;
     if (active)
       load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
@@ -864,7 +875,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ 
 // Exact merge of the fallback's per-split top-K keys of each listed row.
 // Persistent over the list. A listed row always has >= K candidates (it is
 // longer than K); fewer means a selector failure and fails the row closed.
-template <int K, int FBS>
+template <int K, int FBS, int FBS_MIN>
 __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const int32_t* __restrict__ page_table,
                                                              int64_t P_log, int32_t* __restrict__ out_raw,
                                                              int32_t* __restrict__ out_slot,
@@ -877,12 +888,13 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
   __shared__ BlockScratch<NT> s_red;
   __shared__ int32_t s_n, s_total;
   const int listed = *c.fb_count;
+  const int fbs = fallback_splits(listed, FBS, FBS_MIN);   // as the scan chose
   for (int li = blockIdx.x; li < listed; li += gridDim.x) {
     const int64_t row = c.fb_list[li];
     const uint64_t* keys = c.cand + static_cast<size_t>(row) * c.cap;
     if (threadIdx.x == 0) {
       int total = 0;
-      for (int i = 0; i < FBS; ++i) {
+      for (int i = 0; i < fbs; ++i) {
         s_cnt[i] = c.fb_cnt[static_cast<size_t>(row) * 4 + i];
         if (s_cnt[i] < 0 || s_cnt[i] > K) total = -1000000;
         total += s_cnt[i];
@@ -904,9 +916,9 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
     };
     bool ok = true;
     uint64_t T = 0;
-    if (s_total > K) T = block_radix_select<NT, 8>(src, static_cast<int64_t>(FBS) * K, K, s_hist, s_red, &ok);
+    if (s_total > K) T = block_radix_select<NT, 8>(src, static_cast<int64_t>(fbs) * K, K, s_hist, s_red, &ok);
     if (ok) {
-      for (int e = threadIdx.x; e < FBS * K; e += NT) {
+      for (int e = threadIdx.x; e < fbs * K; e += NT) {
         uint64_t x;
         if (src(e, x) && x >= T) {
           const int at = atomicAdd(&s_n, 1);
@@ -1300,6 +1312,7 @@ __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restric
 
 static_assert(Geometry<512>::kFbSplits * 512 <= Geometry<512>::kCap, "fallback keys fit the candidate buffer");
 static_assert(Geometry<1024>::kFbSplits * 1024 <= Geometry<1024>::kCap, "fallback keys fit the candidate buffer");
+static_assert(Geometry<512>::kFbSplits <= 4 && Geometry<1024>::kFbSplits <= 4, "fb_cnt holds 4 counts per row");
 
 // ---------------------------------------------------------------------------
 // Launchers
@@ -1372,10 +1385,10 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
           g.row_state, c, p.page_table, p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
       break;
     case 3:
-      fallback_scan_kernel<K, kPoolCap, G::kFbSplits><<<dim3(kFallbackGrid), dim3(kCtaThreads), 0, st>>>(a, c);
+      fallback_scan_kernel<K, kPoolCap, G::kFbSplits, G::kFbSplitsMin><<<dim3(kFallbackGrid), dim3(kCtaThreads), 0, st>>>(a, c);
       break;
     default:
-      fallback_merge_kernel<K, G::kFbSplits><<<dim3(kFallbackGrid), dim3(256), 0, st>>>(
+      fallback_merge_kernel<K, G::kFbSplits, G::kFbSplitsMin><<<dim3(kFallbackGrid), dim3(256), 0, st>>>(
           c, p.page_table, p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
       break;
   }

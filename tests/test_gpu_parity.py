@@ -188,6 +188,27 @@ def test_prefilter_off_and_forced_underfill_give_identical_outputs(K):
     assert mqa.mqa_fp4_status() == 0
 
 
+@pytest.mark.parametrize("K", [512, 1024])
+def test_forced_fallback_on_a_long_list_equals_gated(K):
+    """A list of more than 512 fallback rows runs with fewer splits per row
+    (less merge work) than a short one; both give the gated outputs bit for bit
+    (the short list is covered above, at 20 rows)."""
+    _need_gpu()
+    Q, S = 600, 4096
+    rng = np.random.default_rng(640 + K)
+    st = rng.integers(0, 1000, Q).astype(np.int32)
+    en = np.minimum(st + rng.integers(K + 1, S, Q), S).astype(np.int32)
+    inp = synth.make_inputs(Q, S, K, 6400 + K, row_start=st, row_end=en, P_phys=S // 64 + 1)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K)
+    check_rows(inp, synth.sample_rows(inp, 24, seed=K), *base, where=f"long list K={K}")
+    for flags in (mqa.FLAG_FORCE_UNDERFILL, mqa.FLAG_NO_PREFILTER):
+        got = gu.run_fused(dev, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+    assert mqa.mqa_fp4_status() == 0
+
+
 def test_long_windows_use_the_gate_and_match_the_oracle():
     """Windows long enough for a calibrated gate (many sampled score blocks),
     with ties and duplicates, across several splits."""
