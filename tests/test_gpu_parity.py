@@ -497,6 +497,44 @@ def test_logits_selector_total_order_on_special_value_arrays(S, lo, hi):
                 assert np.array_equal(got[~isnan], ref[~isnan]) and np.all(np.isnan(score[r][isnan]))
 
 
+def test_position_sort_on_clustered_selections():
+    """The emit orders a row's selection by position with position buckets
+    between its smallest and largest position; selections packed into a few
+    buckets (K-1 adjacent positions and one far away), spread evenly, or
+    sitting at both ends of a wide window must all come out in ascending
+    order, equal to the oracle's. Logits are caller-given, so the selector
+    gathers its keys out of position order and always sorts them."""
+    _need_gpu()
+    import torch
+    S = 262144
+    rng = np.random.default_rng(909)
+    Q = 6
+    lg = (rng.standard_normal((Q, S)) * 0.01).astype(np.float32)
+    st = np.array([0, 0, 5, 0, 1000, 0], np.int32)
+    en = np.array([S, S, S - 3, S, S, 40000], np.int32)
+    pt = rng.permutation(S // 64).astype(np.int32)
+    for K in (512, 1024):
+        x = lg.copy()
+        x[0, 100:100 + K - 1] = 5.0 + np.arange(K - 1, dtype=np.float32) * 1e-3   # K-1 adjacent ...
+        x[0, S - 1] = 9.0                                                         # ... and one far away
+        x[1, ::S // K] = 7.0                                                      # evenly spread
+        x[2, 5:5 + K // 2] = 6.0                                                  # half at each end
+        x[2, S - 3 - K // 2:S - 3] = 6.0
+        x[3, 200000:200000 + K] = 3.0                                             # one block far from 0
+        x[4, 1000] = 8.0                                                          # start and a tail
+        x[4, S - K + 1:] = 4.0
+        x[5] = 1.0                                                                # all tied: first K by index
+        outs = mqa.alloc_outputs(Q, K, "cuda", with_score=True)
+        mqa.mqa_fp4_logits_topk(torch.from_numpy(x).cuda(), torch.from_numpy(pt).cuda(), S // 64,
+                                torch.from_numpy(st).cuda(), torch.from_numpy(en).cuda(), K, *outs)
+        raw, slot, cnt, score = [t.cpu().numpy() for t in outs]
+        for r in range(Q):
+            c, want = oracle.select_topk(x[r, st[r]:en[r]].astype(np.float64), int(st[r]), K)
+            assert cnt[r] == c and np.array_equal(raw[r], want), (K, r)
+            assert np.all(np.diff(raw[r]) > 0), (K, r)
+            assert np.array_equal(slot[r], expected_slots(want, pt)), (K, r)
+
+
 # --- the benchmark workloads at full size, sampled rows -------------------------------------
 
 # 256 sampled rows (4x the 64 that the long prefills' workload definitions name)
