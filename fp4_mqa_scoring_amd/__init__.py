@@ -27,6 +27,7 @@ STATUS_BAD_WINDOW, STATUS_BAD_PAGE, STATUS_UNDERFILL, STATUS_SELECTOR = 1, 2, 4,
 FLAG_SPLITS_MASK = 0xFF
 FLAG_NO_PREFILTER = 0x100
 FLAG_FORCE_UNDERFILL = 0x200
+FLAG_NO_FALLBACK = 0x400
 
 
 class MQAError(RuntimeError):

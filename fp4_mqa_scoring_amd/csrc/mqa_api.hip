@@ -220,9 +220,11 @@ int32_t hip_rc(hipError_t e) {
 
 int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   if (p.K != 512 && p.K != 1024) return MQA_ERR_UNSUPPORTED_K;
-  const uint32_t known = MQA_FLAG_SPLITS_MASK | MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL;
+  const uint32_t known =
+      MQA_FLAG_SPLITS_MASK | MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL | MQA_FLAG_NO_FALLBACK;
   if (flags & ~known) return MQA_ERR_BAD_FLAGS;
-  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
+  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & (MQA_FLAG_FORCE_UNDERFILL | MQA_FLAG_NO_FALLBACK)))
+    return MQA_ERR_BAD_FLAGS;
   int32_t rc = check_sizes(p.Q, p.P_phys, p.P_log);
   if (rc != MQA_OK) return rc;
   const bool rows = p.Q > 0;
@@ -257,7 +259,7 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   rc = hip_rc(mqa::launch_row_prep(p, 0, g.row_state, g.fb_count, st));
   record_stage(1, st);
   for (int stage = 0; stage < 5 && rc == MQA_OK; ++stage) {
-    rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_mode, stage, st));
+    rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_mode, (flags & MQA_FLAG_NO_FALLBACK) != 0, stage, st));
     if (stage <= 1) record_stage(2 + stage, st);   // after calibration, after the scan
   }
   record_stage(4, st);
@@ -525,8 +527,9 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
                             void* workspace, int64_t workspace_bytes, int32_t splits, uint32_t flags,
                             void* stream) {
   if (K != 512 && K != 1024) return MQA_ERR_UNSUPPORTED_K;
-  if (flags & ~(MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
-  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & MQA_FLAG_FORCE_UNDERFILL)) return MQA_ERR_BAD_FLAGS;
+  if (flags & ~(MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL | MQA_FLAG_NO_FALLBACK)) return MQA_ERR_BAD_FLAGS;
+  if ((flags & MQA_FLAG_NO_PREFILTER) && (flags & (MQA_FLAG_FORCE_UNDERFILL | MQA_FLAG_NO_FALLBACK)))
+    return MQA_ERR_BAD_FLAGS;
   const int mode = (flags & MQA_FLAG_NO_PREFILTER) ? 1 : (flags & MQA_FLAG_FORCE_UNDERFILL) ? 2 : 0;
   int32_t rc = check_sizes(num_rows, num_phys_pages, max_pages);
   if (rc != MQA_OK) return rc;
@@ -555,7 +558,9 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
   record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, w.fb_count, st));
   record_stage(1, st);
-  if (rc == MQA_OK) rc = hip_rc(mqa::launch_decode(p, w, sp, mode, st, t_stage_events ? record_stage : nullptr));
+  if (rc == MQA_OK)
+    rc = hip_rc(mqa::launch_decode(p, w, sp, mode, (flags & MQA_FLAG_NO_FALLBACK) != 0, st,
+                                   t_stage_events ? record_stage : nullptr));
   record_stage(4, st);
   return rc;
 }

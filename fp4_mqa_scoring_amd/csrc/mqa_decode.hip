@@ -73,6 +73,7 @@ struct DecArgs {
   int32_t splits;
   DecodeScratch w;
   int32_t cap;        // candidate keys per row
+  int32_t no_fallback;   // fail closed instead of listing rows for the fallback
 };
 
 __device__ __forceinline__ void vm_wait_all() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -332,6 +333,11 @@ __global__ void __launch_bounds__(1024) decode_gmerge_kernel(DecArgs a, int32_t*
   if (a.row_state[row] != kRowLong) return;
   const uint32_t n = a.w.cand_n[row];
   if (n > static_cast<uint32_t>(a.cap) || n < static_cast<uint32_t>(K)) {
+    if (a.no_fallback) {   // fail closed: underfill (fewer than K above the gate) or overflow
+      fail_row<K, NT>(row, n < static_cast<uint32_t>(K) ? kCodeUnderfill : kCodeSelector, out_raw, out_slot,
+                      out_count, out_score, status);
+      return;
+    }
     if (threadIdx.x == 0) a.w.fb_list[atomicAdd(a.w.fb_count, 1)] = static_cast<int32_t>(row);
     return;
   }
@@ -438,17 +444,19 @@ __global__ void __launch_bounds__(1024) decode_fb_merge_kernel(DecArgs a, int32_
     const uint64_t* keys = a.w.keys + static_cast<size_t>(row) * splits * K;
     if (threadIdx.x == 0) {
       int total = 0;
+      bool bad = false;
       for (int i = 0; i < splits; ++i) {
         s_cnt[i] = a.w.counts[static_cast<size_t>(row) * splits + i];
-        if (s_cnt[i] < 0 || s_cnt[i] > K) total = -1000000;
+        bad |= s_cnt[i] < 0 || s_cnt[i] > K;
         total += s_cnt[i];
       }
-      s_total = total;
+      s_total = bad ? -1 : total;
       s_n = 0;
     }
     __syncthreads();
-    if (s_total < K) {   // a long row holds more than K positions: anything else is a selector failure
-      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, status);
+    if (s_total < K) {   // a split's selector failed (-1), or fewer than K keys survived: fail closed
+      fail_row<K, NT>(row, s_total < 0 ? kCodeSelector : kCodeUnderfill, out_raw, out_slot, out_count, out_score,
+                      status);
       __syncthreads();
       continue;
     }
@@ -534,8 +542,8 @@ DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t sp
   return w;
 }
 
-hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st,
-                         StageMark mark) {
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, bool no_fallback,
+                         hipStream_t st, StageMark mark) {
   if (p.Q == 0) return hipSuccess;
   int32_t* status = status_word();
   if (status == nullptr) return hipErrorInvalidSymbol;
@@ -556,6 +564,7 @@ hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t spli
   a.splits = splits;
   a.w = w;
   a.cap = candidate_cap(p.K);
+  a.no_fallback = no_fallback ? 1 : 0;
   if (p.K == 512) launch_decode_k<512>(a, p, mode, status, st, mark);
   else launch_decode_k<1024>(a, p, mode, status, st, mark);
   return hipGetLastError();

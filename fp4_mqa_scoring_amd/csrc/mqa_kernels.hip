@@ -126,6 +126,7 @@ struct CandArgs {
   int32_t* fb_count;     // [1]
   int32_t* fb_cnt;       // [Q, 4] per (row, fallback split) key counts
   int32_t cap;
+  int32_t no_fallback;   // fail closed instead of listing rows for the fallback
 };
 
 template <int K>
@@ -819,6 +820,11 @@ __global__ void __launch_bounds__(256) merge_kernel(const int32_t* __restrict__ 
   if (row_state[row] != kRowLong) return;
   const uint32_t n = c.count[row];
   if (n > static_cast<uint32_t>(c.cap) || n < static_cast<uint32_t>(K)) {
+    if (c.no_fallback) {   // fail closed: underfill (fewer than K above the gate) or overflow
+      fail_row<K, NT>(row, n < static_cast<uint32_t>(K) ? kCodeUnderfill : kCodeSelector, out_raw, out_slot,
+                      out_count, out_score, &g_status);
+      return;
+    }
     if (threadIdx.x == 0) c.fb_list[atomicAdd(c.fb_count, 1)] = static_cast<int32_t>(row);
     return;
   }
@@ -894,17 +900,19 @@ __global__ void __launch_bounds__(256) fallback_merge_kernel(CandArgs c, const i
     const uint64_t* keys = c.cand + static_cast<size_t>(row) * c.cap;
     if (threadIdx.x == 0) {
       int total = 0;
+      bool bad = false;
       for (int i = 0; i < fbs; ++i) {
         s_cnt[i] = c.fb_cnt[static_cast<size_t>(row) * 4 + i];
-        if (s_cnt[i] < 0 || s_cnt[i] > K) total = -1000000;
+        bad |= s_cnt[i] < 0 || s_cnt[i] > K;
         total += s_cnt[i];
       }
-      s_total = total;
+      s_total = bad ? -1 : total;
       s_n = 0;
     }
     __syncthreads();
-    if (s_total < K) {
-      fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
+    if (s_total < K) {   // a split's selector failed (-1), or fewer than K keys survived: fail closed
+      fail_row<K, NT>(row, s_total < 0 ? kCodeSelector : kCodeUnderfill, out_raw, out_slot, out_count, out_score,
+                      &g_status);
       __syncthreads();
       continue;
     }
@@ -1276,8 +1284,9 @@ __global__ void __launch_bounds__(256) tile_emit_kernel(const int32_t* __restric
   const int64_t row = blockIdx.x;
   if (row_state[row] != kRowLong) return;
   const int c = run_count[row];
-  if (c < K || c > CAP) {   // a long row visits more than K positions: anything else is a failure
-    fail_row<K, NT>(row, kCodeSelector, out_raw, out_slot, out_count, out_score, &g_status);
+  if (c < K || c > CAP) {   // -1: a compaction failed; fewer than K keys: underfill; both fail closed
+    fail_row<K, NT>(row, c >= 0 && c < K ? kCodeUnderfill : kCodeSelector, out_raw, out_slot, out_count, out_score,
+                    &g_status);
     return;
   }
   const uint64_t* run = pool + static_cast<size_t>(row) * CAP;
@@ -1335,7 +1344,7 @@ static ScanArgs scan_args(const PathArgs& p, const int32_t* row_state, int32_t s
   return a;
 }
 
-static CandArgs cand_args(const GatedScratch& g, int K) {
+static CandArgs cand_args(const GatedScratch& g, int K, bool no_fallback) {
   CandArgs c;
   c.gate = g.gate;
   c.count = g.count;
@@ -1344,6 +1353,7 @@ static CandArgs cand_args(const GatedScratch& g, int K) {
   c.fb_count = g.fb_count;
   c.fb_cnt = g.fb_cnt;
   c.cap = candidate_cap(K);
+  c.no_fallback = no_fallback ? 1 : 0;
   return c;
 }
 
@@ -1357,10 +1367,10 @@ hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int3
 
 template <int K>
 static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
-                                 int stage, hipStream_t st) {
+                                 bool no_fallback, int stage, hipStream_t st) {
   using G = Geometry<K>;
   const ScanArgs a = scan_args(p, g.row_state, splits);
-  const CandArgs c = cand_args(g, K);
+  const CandArgs c = cand_args(g, K, no_fallback);
   const unsigned tiles = static_cast<unsigned>((p.Q + kRowsPerCta - 1) / kRowsPerCta);
   switch (stage) {
     case 0: {
@@ -1395,11 +1405,11 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
   return hipGetLastError();
 }
 
-hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode, int stage,
-                              hipStream_t st) {
+hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
+                              bool no_fallback, int stage, hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
-  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_mode, stage, st)
-                    : launch_gated_k<1024>(p, g, splits, calib_mode, stage, st);
+  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_mode, no_fallback, stage, st)
+                    : launch_gated_k<1024>(p, g, splits, calib_mode, no_fallback, stage, st);
 }
 
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,

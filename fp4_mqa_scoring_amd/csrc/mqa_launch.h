@@ -57,9 +57,10 @@ constexpr int tile_pool_cap(int K) { return 2 * K; }
 hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int32_t* fb_count, hipStream_t st);
 // Stages of the gated fused path: 0 calibration (calib_mode 0 normal, 1 no
 // prefilter, 2 forced underfill), 1 gated scan, 2 merge, 3 fallback scan,
-// 4 fallback merge.
-hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode, int stage,
-                              hipStream_t st);
+// 4 fallback merge. With no_fallback the merge fails closed the rows it would
+// list for the fallback (underfill -3, overflow -4) and the list stays empty.
+hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
+                              bool no_fallback, int stage, hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
                               hipStream_t st);
 // Decode / multi-sequence path: per-wave streaming exact TopK over each row's
@@ -79,9 +80,10 @@ size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
 // Measurement marker called between launches (index, stream); may be null.
 typedef void (*StageMark)(int, hipStream_t);
-// mode 0 gated, 1 no prefilter (every long row takes the exact fallback), 2 forced underfill.
-hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, hipStream_t st,
-                         StageMark mark = nullptr);
+// mode 0 gated, 1 no prefilter (every long row takes the exact fallback), 2 forced underfill;
+// no_fallback: rows the gated pass cannot finish fail closed instead (as for the prefill path).
+hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, bool no_fallback,
+                         hipStream_t st, StageMark mark = nullptr);
 
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.

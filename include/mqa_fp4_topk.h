@@ -81,8 +81,12 @@ extern "C" {
 /* ---- per-row codes in out_count -------------------------------------------- */
 #define MQA_ROW_BAD_WINDOW (-1)      /* start < 0, end < start or end > 64 * P_log */
 #define MQA_ROW_BAD_PAGE (-2)        /* a page touched by the window maps outside [0, P_phys) */
-#define MQA_ROW_UNDERFILL (-3)       /* fewer than K candidates survived and the fallback failed */
-#define MQA_ROW_SELECTOR (-4)        /* internal selection invariant violated */
+#define MQA_ROW_UNDERFILL (-3)       /* fewer than K candidates survived the candidate gate and no exact
+                                        recomputation supplied the rest (MQA_FLAG_NO_FALLBACK), or an
+                                        exact recomputation itself ended with fewer than K keys */
+#define MQA_ROW_SELECTOR (-4)        /* the row's candidates overflowed their bounded buffer and were
+                                        not recomputed (MQA_FLAG_NO_FALLBACK), or an internal selection
+                                        invariant was violated */
 
 /* ---- sticky status bits ---------------------------------------------------- */
 #define MQA_STATUS_BAD_WINDOW 1
@@ -96,6 +100,14 @@ extern "C" {
                                         exact ungated streaming path */
 #define MQA_FLAG_FORCE_UNDERFILL 0x200u /* gate above every key, so every long row underfills
                                            and takes the fallback (for tests) */
+#define MQA_FLAG_NO_FALLBACK 0x400u  /* no exact recomputation of rows the gated pass cannot finish:
+                                        an underfilled row fails closed with MQA_ROW_UNDERFILL
+                                        (status MQA_STATUS_UNDERFILL), an overflowed one with
+                                        MQA_ROW_SELECTOR (status MQA_STATUS_SELECTOR); with
+                                        MQA_FLAG_FORCE_UNDERFILL every long row fails closed (for
+                                        tests of the fail-closed path, PR 5309 Implementation: fail
+                                        closed on underfill); not combinable with
+                                        MQA_FLAG_NO_PREFILTER */
 
 /*
  * Fused FP4 scoring + exact TopK + page mapping (the hot path).

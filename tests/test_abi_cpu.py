@@ -63,8 +63,9 @@ def test_unsupported_k_rejected_before_any_device_work(lib, K):
 
 
 def test_bad_flags_sizes_nulls_alignment_rejected_on_host(lib):
-    assert _call_prefill(lib, flags=0x400) == -8
+    assert _call_prefill(lib, flags=0x800) == -8                # unknown bit
     assert _call_prefill(lib, flags=0x300) == -8                # no prefilter + forced underfill
+    assert _call_prefill(lib, flags=0x500) == -8                # no prefilter + no fallback
     assert _call_prefill(lib, Q=-1) == -4
     assert _call_prefill(lib, P_log=(1 << 31) // 64) == -4
     assert _call_prefill(lib, P_phys=(1 << 31) // 64 + 1) == -4
@@ -142,6 +143,8 @@ def test_decode_entry_checks_arguments_on_host(lib):
     assert call(K=100) == -1
     assert call(flags=0x3) == -8                     # split bits belong to the splits argument
     assert call(flags=0x300) == -8                   # no prefilter + forced underfill
+    assert call(flags=0x500) == -8                   # no prefilter + no fallback
+    assert call(flags=0x800) == -8                   # unknown bit
     assert call(splits=65) == -4
     assert call(splits=-1) == -4
     assert call(ws_bytes=-1) == -4

@@ -202,3 +202,39 @@ def test_windows_beyond_the_sample_budget(K):
     check_decode(d, res, where=f"decode beyond the sample budget K={K}")
     assert np.all(res[2] == K)
     assert mqa.mqa_fp4_status() == 0
+
+
+@pytest.mark.parametrize("K", [512, 1024])
+def test_underfill_without_fallback_fails_closed(K):
+    """As for the prefill path: with MQA_FLAG_NO_FALLBACK a forced underfill
+    fails every long row closed (all -1, NaN scores, count -3, underfill bit),
+    short rows and a row of an invalid sequence are answered as always, and
+    without the forced underfill the outputs equal the default run's."""
+    _need_gpu()
+    d = synth.make_decode_inputs(6, 2, K // 3, 9000, K, seed=57 + K)
+    d.seq_of_row[4] = d.seq_of_row.max() + 5                   # invalid sequence: code -1
+    d.row_end[2] = d.row_start[2] + K // 2                      # a short row
+    t = _dev(d)
+    mqa.mqa_fp4_status()
+    base = run_decode(t, K)
+    st0 = mqa.mqa_fp4_status()
+    assert st0 == mqa.STATUS_BAD_WINDOW
+    got = run_decode(t, K, flags=mqa.FLAG_NO_FALLBACK)
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert mqa.mqa_fp4_status() == st0
+    raw, slot, cnt, score = run_decode(t, K, flags=mqa.FLAG_NO_FALLBACK | mqa.FLAG_FORCE_UNDERFILL)
+    assert mqa.mqa_fp4_status() == st0 | mqa.STATUS_UNDERFILL
+    n = d.row_end.astype(np.int64) - d.row_start.astype(np.int64)
+    n_failed = 0
+    for r in range(d.Q):
+        if r == 4:
+            assert cnt[r] == -1 and np.all(raw[r] == -1) and np.all(slot[r] == -1)
+        elif n[r] <= K:
+            assert cnt[r] == base[2][r] and np.array_equal(raw[r], base[0][r])
+            assert np.array_equal(slot[r], base[1][r])
+        else:
+            assert cnt[r] == mqa.ROW_UNDERFILL, (r, cnt[r])
+            assert np.all(raw[r] == -1) and np.all(slot[r] == -1) and np.all(np.isnan(score[r]))
+            n_failed += 1
+    assert n_failed >= 4

@@ -368,6 +368,78 @@ def test_checker_enforces_index_tie_break():
         check_long_row(sigma, np.abs(sigma), 0, 2, wrong, oracle.check.expected_slots(wrong, pt), 2, pt)
 
 
+def _tau_row(n=400, K=32, seed=3, spread=None, mag_factor=1.5):
+    """Synthetic oracle scores with known magnitudes, the K-th largest tau, and
+    the exact top-K positions (start 0)."""
+    rng = np.random.default_rng(seed)
+    sigma = rng.normal(100.0, 30.0, n)
+    mag = np.abs(sigma) * mag_factor
+    if spread is not None:
+        sigma[-1] = spread                          # one far-away score that sets the window maximum
+        mag[-1] = abs(spread)
+    order = np.argsort(-sigma, kind="stable")
+    top = np.sort(order[:K])
+    tau = sigma[order[K - 1]]
+    return sigma, mag, top, order, tau
+
+
+@pytest.mark.parametrize("mag_factor", [1.0, 1.5])
+def test_checker_swap_band_is_per_score(mag_factor):
+    """Near the K-th score tau a swap is allowed only within the two scores' own
+    bounds e(s) = 1e-5 * max(|s|, m_s): with m = |s| (no cancellation) a selected
+    score 2.1e-5 * tau below tau is rejected and one 1.9e-5 * tau below is
+    accepted; with m = 1.5 |s| the band scales with m."""
+    from oracle.check import score_bound
+    pt = np.arange(64, dtype=np.int32)
+    K = 32
+    sigma, mag, top, order, tau = _tau_row(K=K, mag_factor=mag_factor)
+    check_long_row(sigma, mag, 0, K, top, oracle.check.expected_slots(top, pt), K, pt)
+    kth, nxt = order[K - 1], order[K]
+    for frac, ok in ((0.95, True), (1.05, False)):
+        s = sigma.copy()
+        m = mag.copy()
+        m[nxt] = mag_factor * tau                   # the swapped-in score's magnitude, about tau's
+        band = float(score_bound(tau, mag[kth]) + score_bound(tau, m[nxt]))
+        if mag_factor == 1.0:
+            assert abs(band - 2e-5 * tau) < 1e-12 * tau
+        s[nxt] = tau - frac * band                  # |s| < m[nxt], so e(nxt) is 1e-5 * m[nxt]
+        swapped = np.sort(np.concatenate([top[top != kth], [nxt]]))
+        args = (s, m, 0, K, swapped, oracle.check.expected_slots(swapped, pt), K, pt)
+        if ok:
+            check_long_row(*args)
+        else:
+            with pytest.raises(SelectionMismatch):
+                check_long_row(*args)
+
+
+def test_checker_band_does_not_widen_with_the_window_maximum():
+    """A window holding one very large score: the old window-wide band (2e-5 *
+    the window's maximum magnitude) would allow swaps far below tau; the
+    per-score band does not."""
+    pt = np.arange(64, dtype=np.int32)
+    K = 32
+    sigma, mag, top, order, tau = _tau_row(K=K, spread=1e7)
+    kth, far = order[K - 1], order[K + 40]            # well below tau, inside 2e-5 * 1e7 = 200
+    assert tau - sigma[far] < 2e-5 * 1e7
+    swapped = np.sort(np.concatenate([top[top != kth], [far]]))
+    with pytest.raises(SelectionMismatch):
+        check_long_row(sigma, mag, 0, K, swapped, oracle.check.expected_slots(swapped, pt), K, pt)
+
+
+def test_check_scores_bound_is_per_score():
+    from oracle.check import check_scores, score_bound
+    sigma = np.array([1000.0, -5.0, 0.0, 3.0])
+    mag = np.array([1000.0, 400.0, 0.0, 3.0])
+    e = score_bound(sigma, mag)
+    assert np.array_equal(e, 1e-5 * np.array([1000.0, 400.0, 0.0, 3.0]))
+    check_scores(sigma + 0.99 * e * np.array([1, -1, 1, 1]), sigma, mag)
+    for i in range(4):
+        got = sigma.copy()
+        got[i] += 1.01 * e[i] if e[i] > 0 else 1e-30     # a zero score must be exact
+        with pytest.raises(SelectionMismatch):
+            check_scores(got, sigma, mag)
+
+
 # --- geometry printed on the pages ---------------------------------------------------------
 
 def test_page_geometry_golden():
