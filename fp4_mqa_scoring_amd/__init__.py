@@ -28,6 +28,7 @@ FLAG_SPLITS_MASK = 0xFF
 FLAG_NO_PREFILTER = 0x100
 FLAG_FORCE_UNDERFILL = 0x200
 FLAG_NO_FALLBACK = 0x400
+STATIC_SCRATCH_BYTES = 64 << 20          # MQA_STATIC_SCRATCH_BYTES
 
 
 class MQAError(RuntimeError):
@@ -55,6 +56,7 @@ def lib() -> ctypes.CDLL:
         prefill = [P, P, i64, P, P, i64, P, P, i64, P, P, i32, P, P, P]
         L.mqa_fp4_topk_prefill.argtypes = prefill + [P]
         L.mqa_fp4_topk_prefill_ex.argtypes = prefill + [P, u32, P]
+        L.mqa_fp4_topk_prefill_static.argtypes = prefill + [P, u32, P]
         L.mqa_fp4_dense_topk_prefill.argtypes = [P, P, i64, P, P, i64, P, P, i64, P, P, i32, P, P, P, P, P, P]
         L.mqa_fp4_dense_logits.argtypes = [P, P, i64, P, P, i64, P, P, i64, P, P, P, P]
         L.mqa_fp4_logits_topk.argtypes = [P, i64, P, i64, i64, P, P, i32, P, P, P, P, P]
@@ -76,7 +78,8 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_decode_workspace_bytes.argtypes = [i64, i32, i32, i32]
         L.mqa_fp4_decode_workspace_bytes.restype = i64
         L.mqa_fp4_cache_write.argtypes = [P, i64, P, P, i64, i64, P, P, P]
-        for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_dense_topk_prefill",
+        for name in ("mqa_fp4_topk_prefill", "mqa_fp4_topk_prefill_ex", "mqa_fp4_topk_prefill_static",
+                     "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
                      "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events",
                      "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write",
@@ -183,6 +186,21 @@ def mqa_fp4_topk_prefill_ex(q, q_scale, k_pages, k_scale, weights, page_table, r
         _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), _ptr(out_raw), _ptr(out_slot),
         _ptr(out_count), _ptr(out_score), int(flags), _stream(stream, q.device))
     _rc(rc, "mqa_fp4_topk_prefill_ex")
+
+
+def mqa_fp4_topk_prefill_static(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,
+                                out_raw, out_slot, out_count, out_score=None, flags=0, stream=None):
+    """Allocation-free form of mqa_fp4_topk_prefill_ex: scratch from the library's
+    fixed per-device array (STATIC_SCRATCH_BYTES), so the batch is limited to
+    2,045 rows at K = 1024 and 2,726 at K = 512; calls on one device must be
+    ordered (they share the array). Accepts a capturing stream."""
+    Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
+    _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)
+    rc = lib().mqa_fp4_topk_prefill_static(
+        _ptr(q), _ptr(q_scale), Q, _ptr(k_pages), _ptr(k_scale), P_phys, _ptr(weights),
+        _ptr(page_table), P_log, _ptr(row_start), _ptr(row_end), int(K), _ptr(out_raw), _ptr(out_slot),
+        _ptr(out_count), _ptr(out_score), int(flags), _stream(stream, q.device))
+    _rc(rc, "mqa_fp4_topk_prefill_static")
 
 
 def mqa_fp4_dense_topk_prefill(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end, K,

@@ -218,7 +218,35 @@ int32_t hip_rc(hipError_t e) {
   return MQA_ERR_HIP;
 }
 
-int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
+// Scratch of the allocation-free entry point: one fixed array per device, held
+// until the process ends. In host code its name only stands for the variable;
+// the device address of each device's copy comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MQA_STATIC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch` (device `dev` current).
+int32_t static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return MQA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return MQA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MQA_OK;
+}
+
+// The fused path. use_static: scratch from the device's fixed array instead of
+// a stream-ordered allocation (then nothing is allocated and a capturing
+// stream is accepted; every scratch word is written by a kernel of the call
+// before it is read, so the array needs no clearing between calls).
+int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st, bool use_static = false) {
   if (p.K != 512 && p.K != 1024) return MQA_ERR_UNSUPPORTED_K;
   const uint32_t known =
       MQA_FLAG_SPLITS_MASK | MQA_FLAG_NO_PREFILTER | MQA_FLAG_FORCE_UNDERFILL | MQA_FLAG_NO_FALLBACK;
@@ -227,6 +255,8 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
     return MQA_ERR_BAD_FLAGS;
   int32_t rc = check_sizes(p.Q, p.P_phys, p.P_log);
   if (rc != MQA_OK) return rc;
+  const FusedScratch lay = fused_scratch_layout(p.Q, p.K);
+  if (use_static && lay.total > static_cast<size_t>(MQA_STATIC_SCRATCH_BYTES)) return MQA_ERR_BAD_SIZE;
   const bool rows = p.Q > 0;
   const PtrSpec specs[] = {
       {p.q, rows, 16},          {p.q_scale, rows, 4},   {p.k_pages, p.P_phys > 0, 16},
@@ -236,17 +266,26 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st) {
   };
   DeviceGuard guard;
   DeviceInfo info;
-  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info);
+  rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info, /*allow_capture=*/use_static);
   if (rc != MQA_OK) return rc;
   if (!rows) return MQA_OK;
   const int32_t splits = (flags & MQA_FLAG_SPLITS_MASK) ? static_cast<int32_t>(flags & MQA_FLAG_SPLITS_MASK)
                                                         : auto_splits(p.Q, info.cus, 4);
   const int calib_mode = (flags & MQA_FLAG_NO_PREFILTER) ? 1 : (flags & MQA_FLAG_FORCE_UNDERFILL) ? 2 : 0;
-  const FusedScratch lay = fused_scratch_layout(p.Q, p.K);
-  Scratch scratch;
-  rc = scratch.alloc(lay.total, st);
-  if (rc != MQA_OK) return rc;
-  char* base = static_cast<char*>(scratch.p);
+  Scratch allocated;
+  char* base = nullptr;
+  if (use_static) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MQA_ERR_HIP;   // the tensors' device, current since enter()
+    void* ptr = nullptr;
+    rc = static_scratch(dev, &ptr);
+    if (rc != MQA_OK) return rc;
+    base = static_cast<char*>(ptr);
+  } else {
+    rc = allocated.alloc(lay.total, st);
+    if (rc != MQA_OK) return rc;
+    base = static_cast<char*>(allocated.p);
+  }
   mqa::GatedScratch g;
   g.row_state = reinterpret_cast<int32_t*>(base + lay.state_off);
   g.gate = reinterpret_cast<uint64_t*>(base + lay.gate_off);
@@ -291,6 +330,17 @@ int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_
   return run_fused(p, flags, static_cast<hipStream_t>(stream));
 }
 
+int32_t mqa_fp4_topk_prefill_static(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                    const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
+                                    const float* weights, const int32_t* page_table, int64_t num_logical_pages,
+                                    const int32_t* row_start, const int32_t* row_end, int32_t K, int32_t* out_raw,
+                                    int32_t* out_slot, int32_t* out_count, float* out_score, uint32_t flags,
+                                    void* stream) {
+  const PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  page_table,
+                   num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
+  return run_fused(p, flags, static_cast<hipStream_t>(stream), /*use_static=*/true);
+}
+
 int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
                                    const uint8_t* k_pages, const uint8_t* k_scale, int64_t num_phys_pages,
                                    const float* weights, const int32_t* page_table, int64_t num_logical_pages,
@@ -315,10 +365,10 @@ int32_t mqa_fp4_dense_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   if (!rows) return MQA_OK;
   const PathArgs p{q,       q_scale,    num_rows,  k_pages,  k_scale, num_phys_pages, weights,  page_table,
                    num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
-  Scratch scratch;
-  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  Scratch buf;
+  rc = buf.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
-  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  int32_t* row_state = static_cast<int32_t*>(buf.p);
   record_stage(0, st);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   record_stage(1, st);
@@ -350,10 +400,10 @@ int32_t mqa_fp4_dense_logits(const uint8_t* q, const uint8_t* q_scale, int64_t n
   if (!rows) return MQA_OK;
   const PathArgs p{q,       q_scale, num_rows, k_pages, k_scale, num_phys_pages, weights, page_table,
                    num_logical_pages, row_start, row_end, 0, nullptr, nullptr, nullptr, nullptr};
-  Scratch scratch;
-  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  Scratch buf;
+  rc = buf.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
-  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  int32_t* row_state = static_cast<int32_t*>(buf.p);
   rc = hip_rc(mqa::launch_row_prep(p, 1, row_state, nullptr, st));
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_dense_score(p, row_state, auto_splits(num_rows, info.cus), logits, st));
   return rc;
@@ -380,10 +430,10 @@ int32_t mqa_fp4_logits_topk(const float* logits, int64_t num_rows, const int32_t
   if (!rows) return MQA_OK;
   const PathArgs p{nullptr, nullptr, num_rows, nullptr, nullptr, num_phys_pages, nullptr, page_table,
                    num_logical_pages, row_start, row_end, K, out_raw, out_slot, out_count, out_score};
-  Scratch scratch;
-  rc = scratch.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
+  Scratch buf;
+  rc = buf.alloc(align_up(static_cast<size_t>(num_rows) * sizeof(int32_t)), st);
   if (rc != MQA_OK) return rc;
-  int32_t* row_state = static_cast<int32_t*>(scratch.p);
+  int32_t* row_state = static_cast<int32_t*>(buf.p);
   rc = hip_rc(mqa::launch_row_prep(p, 0, row_state, nullptr, st));
   if (rc == MQA_OK) rc = hip_rc(mqa::launch_logits_topk(p, logits, row_state, st));
   return rc;
@@ -461,10 +511,10 @@ int32_t mqa_fp4_tiled_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int
   const size_t floor_b = align_up(Qz * sizeof(uint64_t));
   const size_t run_b = align_up(Qz * static_cast<size_t>(mqa::tile_pool_cap(K)) * sizeof(uint64_t));
   const size_t tile_b = align_up(Qz * static_cast<size_t>(tile_positions) * sizeof(float));
-  Scratch scratch;
-  rc = scratch.alloc(state_b + count_b + floor_b + run_b + tile_b, st);
+  Scratch buf;
+  rc = buf.alloc(state_b + count_b + floor_b + run_b + tile_b, st);
   if (rc != MQA_OK) return rc;
-  char* base = static_cast<char*>(scratch.p);
+  char* base = static_cast<char*>(buf.p);
   int32_t* row_state = reinterpret_cast<int32_t*>(base);
   int32_t* run_count = reinterpret_cast<int32_t*>(base + state_b);
   uint64_t* run_floor = reinterpret_cast<uint64_t*>(base + state_b + count_b);

@@ -136,6 +136,32 @@ int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_
                                 float* out_score, uint32_t flags, void* stream);
 
 /*
+ * Allocation-free form of mqa_fp4_topk_prefill_ex, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, flags, outputs and fail-
+ * closed rules as mqa_fp4_topk_prefill_ex (the same kernels run). The call's
+ * scratch -- mqa_fp4_topk_scratch_bytes(num_rows, K, device) bytes -- comes
+ * from a fixed array of MQA_STATIC_SCRATCH_BYTES bytes that the library keeps
+ * on every device it runs on until the process ends, so num_rows is limited to
+ * what fits: 2,045 rows at K = 1024 and 2,726 at K = 512; a larger batch
+ * returns MQA_ERR_BAD_SIZE with nothing launched. The call allocates and frees
+ * nothing, never synchronises, and accepts a capturing stream (the kernels
+ * write every scratch word before reading it, so replays need no clearing).
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap in time on one device (on streams not
+ * ordered with each other, or from several host threads) race and give
+ * undefined outputs -- order them on one stream.
+ */
+#define MQA_STATIC_SCRATCH_BYTES (64ll << 20)
+int32_t mqa_fp4_topk_prefill_static(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
+                                    const uint8_t* k_pages, const uint8_t* k_scale,
+                                    int64_t num_phys_pages, const float* weights,
+                                    const int32_t* page_table, int64_t num_logical_pages,
+                                    const int32_t* row_start, const int32_t* row_end, int32_t K,
+                                    int32_t* out_raw, int32_t* out_slot, int32_t* out_count,
+                                    float* out_score, uint32_t flags, void* stream);
+
+/*
  * Dense comparator (the legacy full-logits path the pages measure against:
  * PR 5282 Motivation, where the whole fp32 row-by-context score matrix is built
  * first and TopK runs on it afterwards). Writes the fp32 score of every position inside each
