@@ -19,7 +19,10 @@ def declared_symbols():
 @pytest.fixture(scope="module")
 def lib():
     import fp4_mqa_scoring_amd as m
-    if not os.path.exists(m.LIB_PATH):
+    override = os.environ.get("MQA_ABI_TEST_LIB")   # a sanitizer build of the same sources
+    if override:                                     # (tests/test_host_sanitizers.py)
+        m.LIB_PATH = override
+    elif not os.path.exists(m.LIB_PATH):
         from fp4_mqa_scoring_amd import build
         build.build()
     return m.lib()
