@@ -33,8 +33,9 @@ FLOP_PER_MFMA = 2 * 32 * 32 * 64      # one v_mfma_scale_f32_32x32x64_f8f6f4
 VALU_PER_PAIR = 2 * 64                # integer ReLU + fp32 FMA per head
 MXFP4_PEAK = 10.1e15                  # MI355X dense MXFP4 MFMA, FLOP/s
 VALU_PEAK = 157.3e12 / 2              # fp32 vector: 157.3 TFLOP/s = 78.65e12 FMA lane-ops/s
-# On gfx950 a SIMD runs MFMA and VALU work one after the other, so the scorer's
-# ceiling is the sum of both times per pair.
+# On gfx950 a SIMD runs MFMA and VALU work largely one after the other (the issue
+# probe measures how little of it overlaps), so the scorer's ceiling at the
+# published rates is the sum of both times per pair.
 SERIAL_PAIR_S = FLOP_PER_PAIR / MXFP4_PEAK + VALU_PER_PAIR / VALU_PEAK
 HBM_PEAK = 8.0e12
 PAGES_LITETOPK_MS = {  # PR 5309 Validation table, MI355X, LiteTopK column
@@ -323,16 +324,26 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size first (for counter scaling)")
     ap.add_argument("--splits", type=int, default=0, help="override context splits (0 = automatic)")
-    ap.add_argument("--op", default="topk", choices=("topk", "quantize", "decode"),
+    ap.add_argument("--op", default="topk", choices=("topk", "quantize", "decode", "probe"),
                     help="topk: the fused operator (default); quantize: the MXFP4 quantiser and the C4 cache "
                          "writer on the headline call's query tensor and cache; decode: the multi-sequence "
-                         "form on a decode batch, timed as HIP graph replays")
-    args = ap.parse_args()
+                         "form on a decode batch, timed as HIP graph replays; probe: the issue and LDS probes "
+                         "alone (for counter runs)")
+    ap.add_argument("--processes", type=int, default=3,
+                    help="fresh processes for --op topk, median reported (the pages' protocol; 1 = this one)")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="also run the probes, the tiled comparator and the CPU baseline (1) or not (0)")
+    argv = sys.argv[1:]
+    args = ap.parse_args(argv)
+    args.passthrough = child_args(argv)
 
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); the operator shards by rows "
               "with no exchange between GPUs, so N GPUs would run N independent row slices", file=sys.stderr)
         sys.exit(2)
+    if args.op == "topk" and args.processes > 1:
+        run_processes(args)
+        return
 
     import torch
     import fp4_mqa_scoring_amd as mqa
@@ -358,6 +369,12 @@ def main():
         return
     if args.op == "decode":
         bench_decode(args, torch, mqa, dev)
+        return
+    if args.op == "probe":
+        from fp4_mqa_scoring_amd import probe
+        out = {"issue_rates": probe.issue_rates(),
+               "lds_read_probe_ms": {p: probe.lds_ms(i) for i, p in enumerate(("scan_image", "linear", "unswizzled"))}}
+        print(json.dumps(out), flush=True)
         return
     cfg = int(args.workload) if args.workload.isdigit() else args.workload
     if cfg not in synth.CONFIGS:
@@ -408,29 +425,14 @@ def main():
     kern_flops = pairs * FLOP_PER_PAIR / (kern * 1e-3)
     kern_valu = pairs * VALU_PER_PAIR / (kern * 1e-3)
 
-    # sustained peaks of this device under the same conditions (outside the timed region)
-    peaks, probe_ms = {}, {}
-    p_blocks, p_iters = 2048, 2000
-    pout = torch.empty(p_blocks * 512, dtype=torch.float32, device=dev)
-    for kind, name, work in ((0, "mxfp4_mfma_tflops", p_blocks * 8 * p_iters * 4 * FLOP_PER_MFMA),
-                             (1, "fp32_fma_tops", p_blocks * 512 * p_iters * 64),
-                             (2, None, 0), (3, None, 0), (4, None, 0), (5, None, 0)):
-        for _ in range(2):
-            mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            mqa.mqa_fp4_peak_probe(kind, pout, p_blocks, p_iters, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        probe_ms[kind] = e0.elapsed_time(e1) / 5
-        if name:
-            peaks[name] = work / (probe_ms[kind] * 1e-3) / 1e12
-    del pout
-    # one MFMA wave and one FMA wave per SIMD: 0 = the SIMD runs the two one after
-    # the other (time = half of each pure run), 1 = fully overlapped (time = the larger half)
-    half_m, half_f = probe_ms[0] / 2, probe_ms[1] / 2
-    overlap = (half_m + half_f - probe_ms[2]) / min(half_m, half_f)
+    # issue rates of this device's SIMDs, in shader cycles (bench-only probe library),
+    # and the LDS read pattern of the score-block image; outside the timed region
+    rates, lds = None, None
+    if args.extras:
+        from fp4_mqa_scoring_amd import probe
+        rates = probe.issue_rates(stream=stream)
+        lds = {"scan_image": probe.lds_ms(0, stream=stream), "linear": probe.lds_ms(1, stream=stream),
+               "unswizzled": probe.lds_ms(2, stream=stream)}
 
     # alternating dense / fused pairs, outside the timed region
     dense = None
@@ -465,7 +467,7 @@ def main():
 
     # alternating context-tiled / fused pairs, outside the timed region
     tiled = None
-    if args.tiled_pairs > 0:
+    if args.tiled_pairs > 0 and args.extras:
         t_out = mqa.alloc_outputs(Q, K, dev)
 
         def tiled_call():
@@ -522,19 +524,14 @@ def main():
                      "kernel": f"scan_kernel<{K}>", "kernel_ms": kern,
                      "valu_frac": kern_valu / VALU_PEAK,
                      "mfma_plus_valu_frac": pairs * SERIAL_PAIR_S / (kern * 1e-3),
-                     "measured_peak_tflops": peaks["mxfp4_mfma_tflops"],
-                     "frac_of_measured_peak": kern_flops / 1e12 / peaks["mxfp4_mfma_tflops"],
-                     "measured_fp32_fma_tops": peaks["fp32_fma_tops"],
-                     "mfma_plus_valu_frac_measured": pairs * (FLOP_PER_PAIR / (peaks["mxfp4_mfma_tflops"] * 1e12)
-                                                              + VALU_PER_PAIR / (peaks["fp32_fma_tops"] * 1e12))
-                                                     / (kern * 1e-3),
-                     "simd_mfma_valu_overlap": overlap,
-                     "overlap_probe_ms": {"mfma_only": probe_ms[0], "fma_only": probe_ms[1],
-                                          "one_of_each_per_simd": probe_ms[2]},
+                     "measured_peak_tflops": rates["mxfp4_tflops_measured"] if rates else None,
+                     "frac_of_measured_peak": kern_flops / 1e12 / rates["mxfp4_tflops_measured"] if rates else None,
+                     # shader cycles per SIMD: MFMA and fp32 FMA issue, and how much of the
+                     # shorter of the two hides when one SIMD runs both (0 = none)
+                     "issue_rates": rates,
                      # LDS reads of the score-block image: the scan's pattern vs a linear
                      # (conflict-free) one and the unswizzled image
-                     "lds_read_probe_ms": {"scan_image": probe_ms[3], "linear": probe_ms[4],
-                                           "unswizzled": probe_ms[5]}},
+                     "lds_read_probe_ms": lds},
         "mxfp4_tflops_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / 1e12,
         "mxfp4_peak_frac_per_call": pairs * FLOP_PER_PAIR / (ms_step * 1e-3) / MXFP4_PEAK,
         "stage_ms": {"row_prep": float(np.mean(prep_ms)), "calibration": float(np.mean(calib_ms)),
@@ -548,11 +545,84 @@ def main():
     key = (Q, S, K)
     if key in PAGES_LITETOPK_MS:   # the pages' LiteTopK at this exact shape
         line["vs_baseline"] = PAGES_LITETOPK_MS[key] / ms_step
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and args.extras:
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, seed=1)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
+
+
+def child_args(argv):
+    """The arguments a child process inherits: all but the process options."""
+    out, skip = [], False
+    for a in argv:
+        if skip:
+            skip = False
+            continue
+        if a in ("--processes", "--extras"):
+            skip = True
+            continue
+        if a.startswith("--processes=") or a.startswith("--extras="):
+            continue
+        out.append(a)
+    return out
+
+
+def merge_lines(lines, args):
+    """One line from the children's lines: the first child's, with its time
+    figures replaced by the median over the children and every rate scaled to
+    match; each child's figures listed under "processes"."""
+    line = dict(lines[0])
+    med = lambda xs: float(np.median(xs))
+    ms = med([ln["ms_per_step"] for ln in lines])
+    scale = lines[0]["ms_per_step"] / ms
+    line["value"] = lines[0]["value"] * scale
+    line["ms_per_step"] = ms
+    if line.get("vs_baseline") is not None:
+        line["vs_baseline"] *= scale
+    for k in ("mxfp4_tflops_per_call", "mxfp4_peak_frac_per_call"):
+        if k in line:
+            line[k] *= scale
+    roof = dict(line["roofline"])
+    kms = med([ln["roofline"]["kernel_ms"] for ln in lines])
+    ks = roof["kernel_ms"] / kms
+    for k in ("achieved", "frac", "valu_frac", "mfma_plus_valu_frac", "frac_of_measured_peak"):
+        if roof.get(k) is not None:
+            roof[k] *= ks
+    roof["kernel_ms"] = kms
+    line["roofline"] = roof
+    line["stage_ms"] = {k: med([ln["stage_ms"][k] for ln in lines]) for k in line["stage_ms"]}
+    if line.get("dense_comparator"):
+        line["dense_comparator"] = dict(line["dense_comparator"])
+        for k in ("dense_ms_median", "fused_ms_median"):
+            line["dense_comparator"][k] = med([ln["dense_comparator"][k] for ln in lines])
+        line["dense_comparator"]["dense_equals_fused"] = all(ln["dense_comparator"]["dense_equals_fused"]
+                                                             for ln in lines)
+    line["checks_ok"] = all(ln["checks_ok"] for ln in lines)
+    line["processes"] = [{"ms_per_step": ln["ms_per_step"], "kernel_ms": ln["roofline"]["kernel_ms"],
+                          "dense_ms_median": (ln.get("dense_comparator") or {}).get("dense_ms_median")}
+                         for ln in lines]
+    line["protocol"] = (f"median of {len(lines)} fresh processes; each: {args.warmup} warmup + {args.steps} "
+                        f"timed calls, then 5 warmup + {args.pairs} alternating dense/fused pairs")
+    return line
+
+
+def run_processes(args) -> None:
+    """The pages' protocol ("[FlyDSL] Add FP4 LiteTopK prefill operator",
+    Validation: median of three fresh processes): the same measurement in fresh
+    child processes, started before this process touches the GPU; the first
+    also runs the probes, the tiled comparator and the CPU baseline."""
+    import subprocess
+    lines = []
+    for i in range(args.processes):
+        cmd = [sys.executable, os.path.abspath(__file__), "--processes", "1",
+               "--extras", "1" if i == 0 else "0"] + args.passthrough
+        print(f"bench.py: process {i + 1} of {args.processes}", file=sys.stderr, flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        if r.returncode != 0:
+            sys.exit(r.returncode)
+        lines.append(json.loads(r.stdout.strip().splitlines()[-1]))
+    print(json.dumps(merge_lines(lines, args)), flush=True)
 
 
 if __name__ == "__main__":

@@ -68,7 +68,6 @@ def lib() -> ctypes.CDLL:
         L.mqa_fp4_error_string.restype = ctypes.c_char_p
         L.mqa_fp4_abi_version.argtypes = []
         L.mqa_fp4_set_stage_events.argtypes = [P, i32]
-        L.mqa_fp4_peak_probe.argtypes = [i32, P, i32, i32, P]
         L.mqa_fp4_quantize.argtypes = [P, i64, P, P, P]
         L.mqa_fp4_tiled_topk_prefill.argtypes = prefill[:11] + [i32, i32, P, P, P, P, P]
         L.mqa_fp4_tiled_scratch_bytes.argtypes = [i64, i32, i32]
@@ -82,7 +81,7 @@ def lib() -> ctypes.CDLL:
                      "mqa_fp4_dense_topk_prefill",
                      "mqa_fp4_dense_logits", "mqa_fp4_logits_topk", "mqa_fp4_supported_k",
                      "mqa_fp4_status", "mqa_fp4_abi_version", "mqa_fp4_set_stage_events",
-                     "mqa_fp4_peak_probe", "mqa_fp4_quantize", "mqa_fp4_cache_write",
+                     "mqa_fp4_quantize", "mqa_fp4_cache_write",
                      "mqa_fp4_tiled_topk_prefill", "mqa_fp4_topk_decode"):
             getattr(L, name).restype = i32
         _lib = L
@@ -366,16 +365,6 @@ def mqa_fp4_cache_write(k, positions, page_table, k_pages, k_scale, stream=None)
     _rc(lib().mqa_fp4_cache_write(_ptr(k), n, _ptr(positions), _ptr(page_table), page_table.numel(),
                                   k_pages.shape[0], _ptr(k_pages), _ptr(k_scale), _stream(stream, k.device)),
         "mqa_fp4_cache_write")
-
-
-def mqa_fp4_peak_probe(kind: int, out, blocks: int, iters: int, stream=None) -> None:
-    """Measurement hook: launch the pure MXFP4 MFMA (kind 0) or fp32 FMA (kind 1)
-    peak loop on ``stream``; ``out`` is a float32 device tensor of blocks*512."""
-    if out is not None and out.numel() < int(blocks) * 512:
-        raise MQAError(-4, "mqa_fp4_peak_probe: out holds fewer than blocks*512 floats")
-    _rc(lib().mqa_fp4_peak_probe(int(kind), _ptr(out), int(blocks), int(iters),
-                                 _stream(stream, out.device if out is not None else None)),
-        "mqa_fp4_peak_probe")
 
 
 def mqa_fp4_set_stage_events(events) -> None:

@@ -8,7 +8,10 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmqa_fp4.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mqa_kernels.hip", "mqa_api.hip", "mqa_probe.hip", "mqa_quant.hip", "mqa_decode.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mqa_kernels.hip", "mqa_api.hip", "mqa_quant.hip", "mqa_decode.hip")]
+# measurement probes (bench only), a library of their own beside the operator's
+PROBE_LIB = os.path.join(PKG, "libmqa_fp4_probe.so")
+PROBE_SOURCES = [os.path.join(PKG, "csrc", "mqa_probe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -25,13 +28,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def _build_one(lib: str, sources, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *sources, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Builds the operator library and the bench-only probe library."""
+    _build_one(LIB, SOURCES, verbose)
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 

@@ -234,9 +234,11 @@ __device__ __forceinline__ float score64(const QRow& r, const uint8_t* s_codes,
 // ---------------------------------------------------------------------------
 // Scoring of one 256-position score block for one row, as 8 groups of 32
 // positions (4 MFMAs each, then the ReLU + head-weighted epilogue). On gfx950 a
-// SIMD does not run MFMA and VALU work at the same time, so there is nothing to
-// gain from keeping two groups in flight inside a wave; the register budget goes
-// to occupancy instead (four waves per SIMD hide the MFMA and LDS latencies).
+// SIMD runs MFMA and VALU work largely one after the other (measured: one MFMA
+// wave beside two fp32-FMA waves hides about 15% of the shorter work), so there
+// is little to gain from keeping two groups in flight inside a wave; the
+// register budget goes to occupancy instead (four waves per SIMD hide the MFMA
+// and LDS latencies).
 // The swizzled LDS chunk offsets depend only on lane % 32, so every B-operand
 // address is a per-lane base plus a compile-time offset. Same arithmetic, in the
 // same order, as score64(): the scores are bit-identical.

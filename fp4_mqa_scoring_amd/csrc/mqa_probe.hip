@@ -1,23 +1,26 @@
-// Peak probes: a pure MXFP4 MFMA loop, a pure fp32 FMA loop and the two side by
-// side on every SIMD, launched on the caller's stream so that the sustained
-// rates, and whether a SIMD overlaps the two kinds of work, can be measured
-// under the same clocks and power state the operator runs in (MI355X's
-// published peaks are quoted at 2.4 GHz; the shader clock is lower under dense
-// MFMA load). Three more kinds time LDS read patterns, so that the bank
-// behaviour of the score-block image can be checked on the device.
+// Measurement library beside the operator (libmqa_fp4_probe.so, declared in
+// include/mqa_fp4_probe.h): synthetic loops that measure, in shader cycles per
+// SIMD, the issue rates the scan kernel is built from -- MXFP4 MFMAs, fp32 VALU
+// operations, both side by side on one SIMD -- and the LDS read pattern of the
+// score-block image. No operator work runs here.
 #include "mqa_device.h"
 #include "mqa_fp4_topk.h"
+#include "mqa_fp4_probe.h"
+
+#include <cstring>
 
 namespace mqa {
 namespace {
 
-constexpr int kProbeThreads = 512;
+// One block per CU: the issue probe asks for more LDS than half a CU holds.
+constexpr int kIssueLdsBytes = 96 * 1024;
+constexpr int kLdsProbeThreads = 512;
 
 // Four independent accumulator chains per wave, one 32x32x64 FP4 MFMA each per
-// iteration (2*32*32*64 FLOP). Codes and scales are arbitrary finite values.
+// iteration. Codes and scales are arbitrary finite values.
 __device__ __noinline__ float mfma_loop(int iters, int l) {
   const v4i a = {l * 0x01010101, l * 0x03030303, l * 0x05050505, l * 0x07070707};
-  v4i b = a ^ v4i{0x55555555, 0x33333333, 0x0F0F0F0F, 0x11111111};
+  const v4i b = a ^ v4i{0x55555555, 0x33333333, 0x0F0F0F0F, 0x11111111};
   const int sc = 0x7F7F7F7F;
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
@@ -29,27 +32,46 @@ __device__ __noinline__ float mfma_loop(int iters, int l) {
   return c0[0] + c1[1] + c2[2] + c3[3];
 }
 
-// Eight independent chains, 64 fp32 FMAs per lane per iteration.
+// Sixteen independent chains, 64 fp32 FMAs per lane per iteration.
 __device__ __noinline__ float fma_loop(int iters, int l) {
-  float w[16], x[16], p[8];
+  float w[16], x[16], p[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     w[i] = 1.0f + 0x1p-20f * static_cast<float>(l + i);
     x[i] = 0.5f - 0x1p-21f * static_cast<float>(l * i);
+    p[i] = 0.0f;
   }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) p[c] = 0.0f;
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i & 7] = __builtin_fmaf(w[i], x[(i + r) & 15], p[i & 7]);
-    x[0] = __builtin_fmaf(p[0], 0x1p-100f, x[0]);
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_fmaf(w[i], x[(i + r) & 15], p[i]);
+    __asm__ __volatile__("" : "+v"(x[0]), "+v"(x[5]), "+v"(x[10]));   // no hoisting across iterations
   }
   float s = 0.0f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s += p[c];
+  for (int i = 0; i < 16; ++i) s += p[i];
   return s;
+}
+
+__global__ void __launch_bounds__(1024) issue_probe_kernel(int n_mfma, int iters, uint64_t* __restrict__ rec,
+                                                           float* __restrict__ sink) {
+  extern __shared__ char s_reserve[];   // only reserved: one block per CU
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  if (threadIdx.x == 0) s_reserve[0] = 0;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const float v = (w >> 2) < n_mfma ? mfma_loop(iters, l) : fma_loop(iters, l);
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = v;
+  if (l == 0) {
+    uint64_t* o = rec + (static_cast<size_t>(blockIdx.x) * nw + w) * 3;
+    o[0] = t0;
+    o[1] = t1;
+    // HW_ID (wave slot, SIMD, CU, shader engine) and XCC_ID hardware registers
+    o[2] = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4))) |
+           (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 20))) << 32);
+  }
 }
 
 // Two 16-byte LDS reads per lane per iteration from one of the eight 32-position
@@ -68,57 +90,120 @@ __device__ __forceinline__ float lds_loop(const uint8_t* img, int o0, int o1, in
   return static_cast<float>(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
 }
 
-// kind 0: every wave runs the MFMA loop; 1: every wave the FMA loop; 2: waves
-// 0-3 of the block the MFMA loop and waves 4-7 the FMA loop. Wave w of a block
-// runs on SIMD w % 4, so with kind 2 each SIMD holds one wave of each: its time
-// against half of kind 0's plus half of kind 1's shows whether the SIMD runs
-// MFMA and VALU work at the same time.
-__global__ void __launch_bounds__(kProbeThreads) peak_probe_kernel(int kind, int iters, float* __restrict__ out) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const bool mfma = kind == 0 || (kind == 2 && w < 4);
-  const float v = mfma ? mfma_loop(iters, l) : fma_loop(iters, l);
-  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = v;
-}
-
-// kinds 3-5: LDS reads of a score-block image: 3 the scan's own operand reads
-// (lane_offsets, i.e. with the chunk swizzle), 4 a linear pattern (lane l reads
-// bytes 16 l .. 16 l + 15 of each 1 KB half of a group, free of bank conflicts
-// under any lane grouping), 5 the image without a swizzle. Kind 3 taking the
-// time of kind 4 means the image is read without bank conflicts.
-// Offsets stay inside a group: 3: 31*64 + 48 + 16 = 2048; 4: 1024 + 63*16 + 16
-// = 2048; 5: 31*64 + 32 + 16 + 16 = 2048.
-__global__ void __launch_bounds__(kProbeThreads) lds_probe_kernel(int kind, int iters, float* __restrict__ out) {
+// Offsets stay inside a group: 0: 31*64 + 48 + 16 = 2048; 1: 1024 + 63*16 + 16
+// = 2048; 2: 31*64 + 32 + 16 + 16 = 2048.
+__global__ void __launch_bounds__(kLdsProbeThreads) lds_probe_kernel(int pattern, int iters, float* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint8_t s_img[kProbeImageBytes];
   const int l = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < kProbeImageBytes / 4; i += kProbeThreads)
+  for (int i = threadIdx.x; i < kProbeImageBytes / 4; i += kLdsProbeThreads)
     reinterpret_cast<uint32_t*>(s_img)[i] = static_cast<uint32_t>(i) * 2654435761u;
   __syncthreads();
   int o0, o1;
-  if (kind == 3) {
+  if (pattern == 0) {
     const LaneOffsets lo = lane_offsets(l);
     o0 = lo.code0;
     o1 = lo.code1;
-  } else if (kind == 4) {
+  } else if (pattern == 1) {
     o0 = 16 * l;
     o1 = 1024 + 16 * l;
   } else {
     o0 = (l & 31) * kVecBytes + 32 * (l >> 5);
     o1 = o0 + 16;
   }
-  out[static_cast<size_t>(blockIdx.x) * kProbeThreads + threadIdx.x] = lds_loop(s_img, o0, o1, iters);
+  out[static_cast<size_t>(blockIdx.x) * kLdsProbeThreads + threadIdx.x] = lds_loop(s_img, o0, o1, iters);
 }
+
+// ---- host checks ---------------------------------------------------------------
+
+// The stream's device, made current for the call; restored on scope exit.
+struct Guard {
+  int saved = -1, dev = -1;
+  bool changed = false;
+  int32_t enter(hipStream_t st) {
+    if (hipGetDevice(&saved) != hipSuccess) return MQA_ERR_HIP;
+    dev = saved;
+    if (st != nullptr && hipStreamGetDevice(st, &dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MQA_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MQA_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MQA_ERR_DEVICE;
+    cus = prop.multiProcessorCount;
+    if (dev != saved) {
+      if (hipSetDevice(dev) != hipSuccess) return MQA_ERR_HIP;
+      changed = true;
+    }
+    return MQA_OK;
+  }
+  ~Guard() {
+    if (changed) (void)hipSetDevice(saved);
+  }
+  int cus = 0;
+};
+
+// Device (or managed) memory of device `dev`, with the given alignment.
+int32_t check_out(const void* p, uintptr_t align, int dev) {
+  if (p == nullptr) return MQA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(p) % align) return MQA_ERR_MISALIGNED;
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return MQA_ERR_DEVICE;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return MQA_ERR_DEVICE;
+  return attr.device == dev ? MQA_OK : MQA_ERR_DEVICE;
+}
+
+int32_t launched() { return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP; }
 
 }  // namespace
 }  // namespace mqa
 
-extern "C" int32_t mqa_fp4_peak_probe(int32_t kind, float* out, int32_t blocks, int32_t iters, void* stream) {
-  if (kind < 0 || kind > 5 || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
+extern "C" {
+
+int32_t mqa_probe_blocks(void* stream) {
+  mqa::Guard g;
+  const int32_t rc = g.enter(static_cast<hipStream_t>(stream));
+  return rc == MQA_OK ? g.cus : rc;
+}
+
+int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
+                        void* stream) {
+  if (n_mfma_waves < 0 || n_valu_waves < 0 || n_mfma_waves + n_valu_waves < 1 || n_mfma_waves + n_valu_waves > 4 ||
+      iters < 1)
+    return MQA_ERR_BAD_SIZE;
+  if (rec == nullptr || sink == nullptr) return MQA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(rec) % 8 || reinterpret_cast<uintptr_t>(sink) % 4) return MQA_ERR_MISALIGNED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  mqa::Guard g;
+  int32_t rc = g.enter(st);
+  if (rc != MQA_OK) return rc;
+  if ((rc = mqa::check_out(rec, 8, g.dev)) != MQA_OK || (rc = mqa::check_out(sink, 4, g.dev)) != MQA_OK) return rc;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(mqa::issue_probe_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, mqa::kIssueLdsBytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return MQA_ERR_HIP;
+  }
+  const unsigned threads = 256u * static_cast<unsigned>(n_mfma_waves + n_valu_waves);
+  mqa::issue_probe_kernel<<<dim3(static_cast<unsigned>(g.cus)), dim3(threads), mqa::kIssueLdsBytes, st>>>(
+      n_mfma_waves, iters, rec, sink);
+  return mqa::launched();
+}
+
+int32_t mqa_probe_lds(int32_t pattern, float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (pattern < 0 || pattern > 2 || blocks <= 0 || iters <= 0) return MQA_ERR_BAD_SIZE;
   if (out == nullptr) return MQA_ERR_NULL_POINTER;
   if (reinterpret_cast<uintptr_t>(out) % 4 != 0) return MQA_ERR_MISALIGNED;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (kind <= 2)
-    mqa::peak_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
-  else
-    mqa::lds_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kProbeThreads), 0, st>>>(kind, iters, out);
-  return hipGetLastError() == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+  mqa::Guard g;
+  int32_t rc = g.enter(st);
+  if (rc != MQA_OK) return rc;
+  if ((rc = mqa::check_out(out, 4, g.dev)) != MQA_OK) return rc;
+  mqa::lds_probe_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(mqa::kLdsProbeThreads), 0, st>>>(pattern, iters,
+                                                                                                      out);
+  return mqa::launched();
 }
+
+}  // extern "C"

@@ -1,6 +1,6 @@
 // Block-level selection helpers (exact radix select over unique 64-bit keys,
-// bitonic sort, row emission with the page map) shared by the kernels of the
-// fused, dense, tiled and decode paths.
+// the bucketed position sort, row emission with the page map) shared by the
+// kernels of the fused, dense, tiled and decode paths.
 #pragma once
 
 #include "mqa_device.h"

@@ -126,7 +126,17 @@ int32_t mqa_fp4_topk_prefill(const uint8_t* q, const uint8_t* q_scale, int64_t n
                              void* stream);
 
 /* As mqa_fp4_topk_prefill, plus an optional fp32 score output (NULL = none)
- * and flags (MQA_FLAG_*). Outputs do not depend on the splits chosen. */
+ * and flags (MQA_FLAG_*). Outputs do not depend on the splits chosen.
+ * The flags expose for tests the properties the pages check: the exact merge
+ * of split candidates ("[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
+ * (PR 5282), Changes, and its Validation: exact candidate union) for any
+ * number of context splits; the calibrated candidate filtering of "[FlyDSL]
+ * Add FP4 LiteTopK prefill operator" (PR 5309), Implementation, as a pure
+ * speed-up -- the same TopK sets with it switched off (MQA_FLAG_NO_PREFILTER)
+ * or forced to underfill (MQA_FLAG_FORCE_UNDERFILL); and the same
+ * Implementation's fail-closed rule on underfill (MQA_FLAG_NO_FALLBACK).
+ * out_score holds the fp32 score of each selected position (the fp32 scores
+ * of PR 5282, Motivation). */
 int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows,
                                 const uint8_t* k_pages, const uint8_t* k_scale,
                                 int64_t num_phys_pages, const float* weights,
@@ -223,13 +233,21 @@ int32_t mqa_fp4_logits_topk(const float* logits, int64_t num_rows, const int32_t
 int32_t mqa_fp4_supported_k(int32_t* ks, int32_t capacity, int32_t* n);
 
 /* Bytes of stream-ordered device scratch mqa_fp4_topk_prefill allocates for
- * num_rows rows on `device` (independent of the context length); negative on
- * error. */
+ * num_rows rows on `device`: O(num_rows) bookkeeping plus a bounded candidate
+ * buffer per row, independent of the context length (candidate and merge
+ * scratch independent of the context: "[FlyDSL][DSv4] Prototype FP4 MQA
+ * streaming TopK" (PR 5282), Changes, with its sizes in the MI355X runtime
+ * update; "[AMD][DSv4] Add experimental AITER FP4 streaming TopK", Memory
+ * geometry). Negative on error (MQA_ERR_UNSUPPORTED_K, MQA_ERR_BAD_SIZE,
+ * MQA_ERR_DEVICE for a device that is not a gfx950). */
 int64_t mqa_fp4_topk_scratch_bytes(int64_t num_rows, int32_t K, int32_t device);
 
 /* Synchronises `stream`, then returns in *status the OR of the sticky status
- * bits set by calls on the stream's device since the last read, and clears
- * them. */
+ * bits (MQA_STATUS_*) set by calls on the stream's device since the last read,
+ * and clears them: the device-side half of failing closed ("[FlyDSL] Add FP4
+ * LiteTopK prefill operator" (PR 5309), Implementation), for rows the device
+ * finds invalid or cannot finish. Returns MQA_ERR_NULL_POINTER for a NULL
+ * status, MQA_ERR_DEVICE / MQA_ERR_HIP when the stream or the copy fails. */
 int32_t mqa_fp4_status(void* stream, int32_t* status);
 
 /* Measurement hook. After this call, every fused or dense TopK call made by
@@ -316,26 +334,6 @@ int32_t mqa_fp4_quantize(const float* x, int64_t n_vec, uint8_t* codes, uint8_t*
 int32_t mqa_fp4_cache_write(const float* k, int64_t n, const int32_t* positions, const int32_t* page_table,
                             int64_t num_logical_pages, int64_t num_phys_pages, uint8_t* k_pages, uint8_t* k_scale,
                             void* stream);
-
-/* Measurement hook: sustained-peak probes on `stream` (no operator work).
- * kind 0: a pure MXFP4 MFMA loop, blocks x 8 waves x iters x 4
- *         v_mfma_scale_f32_32x32x64_f8f6f4 (2*32*32*64 FLOP each);
- * kind 1: a pure fp32 FMA loop, blocks x 512 lanes x iters x 64 FMAs;
- * kind 2: in every 512-thread block waves 0-3 run the kind-0 loop and waves
- *         4-7 the kind-1 loop, i.e. one wave of each per SIMD (both halves of
- *         the work of kinds 0 and 1): a time near half of kind 0's plus half of
- *         kind 1's means the SIMD runs MFMA and VALU work one after the other,
- *         near the larger half means it overlaps them;
- * kinds 3-5: LDS read patterns, blocks x 8 waves x iters x 2 ds_read_b128 over
- *         a 16 KB score-block image: 3 the scan's operand reads (with the chunk
- *         swizzle), 4 a linear pattern that no bank grouping makes conflict, 5
- *         the image without a swizzle; kind 3 as fast as kind 4 means the
- *         image is read free of bank conflicts.
- * out: device float[blocks * 512], written once per lane (keeps the work live).
- * MI355X's published peaks are quoted at 2.4 GHz; timing these launches gives
- * the rates under the clocks the operator actually sees. Returns
- * MQA_ERR_BAD_SIZE for another kind or non-positive blocks / iters. */
-int32_t mqa_fp4_peak_probe(int32_t kind, float* out, int32_t blocks, int32_t iters, void* stream);
 
 /* Static description of a return code. */
 const char* mqa_fp4_error_string(int32_t code);

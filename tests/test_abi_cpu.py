@@ -95,14 +95,43 @@ def test_stage_event_hook_takes_exactly_five_events(lib):
     assert lib.mqa_fp4_set_stage_events(None, 0) == 0
 
 
-def test_peak_probe_rejects_bad_arguments_on_host(lib):
+PROBE_HEADER = os.path.join(ROOT, "include", "mqa_fp4_probe.h")
+
+
+@pytest.fixture(scope="module")
+def probe_lib():
+    from fp4_mqa_scoring_amd import build, probe
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    return probe.lib()
+
+
+def test_probes_live_in_their_own_library(lib, probe_lib):
+    """The measurement probes are not part of the operator's ABI: the operator
+    header declares none and its library exports none; the probe header's
+    symbols are all exported by the probe library."""
+    probe_syms = sorted(set(re.findall(r"^\s*int32_t\s+(mqa_probe_\w+)\s*\(", open(PROBE_HEADER).read(), re.M)))
+    assert probe_syms == ["mqa_probe_blocks", "mqa_probe_issue", "mqa_probe_lds"]
+    for name in probe_syms:
+        assert hasattr(probe_lib, name), name
+        assert not hasattr(lib, name), name
+    assert not hasattr(lib, "mqa_fp4_peak_probe")
+    assert not any("probe" in s for s in declared_symbols())
+
+
+def test_probes_reject_bad_arguments_on_host(probe_lib):
     p = ctypes.c_void_p(0x1000)
-    assert lib.mqa_fp4_peak_probe(6, p, 1, 1, None) == -4        # unknown kind
-    assert lib.mqa_fp4_peak_probe(-1, p, 1, 1, None) == -4
-    assert lib.mqa_fp4_peak_probe(0, p, 0, 1, None) == -4        # no blocks
-    assert lib.mqa_fp4_peak_probe(1, p, 1, 0, None) == -4        # no iterations
-    assert lib.mqa_fp4_peak_probe(0, None, 1, 1, None) == -2
-    assert lib.mqa_fp4_peak_probe(0, ctypes.c_void_p(0x1002), 1, 1, None) == -3
+    L = probe_lib
+    assert L.mqa_probe_issue(0, 0, 8, p, p, None) == -4          # no waves
+    assert L.mqa_probe_issue(3, 2, 8, p, p, None) == -4          # more than four waves per SIMD
+    assert L.mqa_probe_issue(-1, 2, 8, p, p, None) == -4
+    assert L.mqa_probe_issue(1, 1, 0, p, p, None) == -4          # no iterations
+    assert L.mqa_probe_issue(1, 1, 8, None, p, None) == -2
+    assert L.mqa_probe_issue(1, 1, 8, ctypes.c_void_p(0x1004), p, None) == -3
+    assert L.mqa_probe_lds(3, p, 1, 1, None) == -4               # unknown pattern
+    assert L.mqa_probe_lds(0, p, 0, 1, None) == -4               # no blocks
+    assert L.mqa_probe_lds(0, None, 1, 1, None) == -2
+    assert L.mqa_probe_lds(0, ctypes.c_void_p(0x1002), 1, 1, None) == -3
 
 
 def test_quantizer_and_cache_writer_reject_bad_arguments_on_host(lib):

@@ -257,16 +257,21 @@ def test_scratch_is_independent_of_context_length():
     assert highs[0] >= mqa.mqa_fp4_topk_scratch_bytes(Q, K), highs
 
 
-def test_peak_probes_run():
-    """The measurement probes launch and write every lane (no operator work)."""
+def test_measurement_probes_run():
+    """The bench-only probes launch on every compute unit, record one span per
+    SIMD, and give plausible issue rates (an MFMA takes tens of cycles, an FMA
+    wave-op a few); a host pointer is refused with MQA_ERR_DEVICE."""
     _need_gpu()
+    import ctypes
     import torch
-    out = torch.full((4 * 512,), float("nan"), dtype=torch.float32, device="cuda:0")
-    for kind in range(6):
-        out.fill_(float("nan"))
-        mqa.mqa_fp4_peak_probe(kind, out, 4, 8)
-        torch.cuda.synchronize()
-        assert torch.isfinite(out).all()
+    from fp4_mqa_scoring_amd import probe
+    r = probe.issue(1, 2, 64)
+    assert r["simds"] == 4 * r["blocks"] > 0
+    rates = probe.issue_rates(iters=256)
+    assert 16 < rates["cycles_per_mfma_2waves"] < 80 and 1 < rates["cycles_per_fma_4waves"] < 8
+    assert probe.lds_ms(0, blocks=64, iters=64) > 0
+    host = torch.zeros(64 * 512, dtype=torch.float32)
+    assert probe.lib().mqa_probe_lds(0, ctypes.c_void_p(host.data_ptr()), 64, 8, None) == -5
 
 
 def test_non_default_stream_gives_same_outputs():
