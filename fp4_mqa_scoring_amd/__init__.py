@@ -191,7 +191,7 @@ def mqa_fp4_topk_prefill_static(q, q_scale, k_pages, k_scale, weights, page_tabl
                                 out_raw, out_slot, out_count, out_score=None, flags=0, stream=None):
     """Allocation-free form of mqa_fp4_topk_prefill_ex: scratch from the library's
     fixed per-device array (STATIC_SCRATCH_BYTES), so the batch is limited to
-    2,045 rows at K = 1024 and 2,726 at K = 512; calls on one device must be
+    1,636 rows at K = 1024 and 2,045 at K = 512; calls on one device must be
     ordered (they share the array). Accepts a capturing stream."""
     Q, P_phys, P_log = _check_inputs(q, q_scale, k_pages, k_scale, weights, page_table, row_start, row_end)
     _check_outputs(Q, K, out_raw, out_slot, out_count, out_score)

@@ -344,7 +344,7 @@ __global__ void __launch_bounds__(1024) decode_gmerge_kernel(DecArgs a, int32_t*
   const uint64_t* keys = a.w.cand + static_cast<size_t>(row) * a.cap;
   if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
-  constexpr int E = (candidate_cap(K) + NT - 1) / NT;   // every candidate in registers (n <= cap)
+  constexpr int E = (decode_candidate_cap(K) + NT - 1) / NT;   // every candidate in registers (n <= cap)
   uint64_t x[E];
   const uint32_t valid = load_keys_regs<NT, E>(keys, static_cast<int>(n), x);
   bool ok = true;
@@ -514,7 +514,7 @@ void launch_decode_k(const DecArgs& a, const PathArgs& p, int mode, int32_t* sta
 
 size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits) {
   const size_t q = static_cast<size_t>(Q), s = static_cast<size_t>(splits);
-  const size_t cap = static_cast<size_t>(candidate_cap(K));
+  const size_t cap = static_cast<size_t>(decode_candidate_cap(K));
   return align256(q * sizeof(int32_t)) + align256(q * s * sizeof(int32_t)) +
          align256(q * s * static_cast<size_t>(K) * sizeof(uint64_t)) + align256(q * sizeof(uint64_t)) +
          align256(q * sizeof(uint32_t)) + align256(q * cap * sizeof(uint64_t)) + align256(q * sizeof(int32_t)) +
@@ -523,7 +523,7 @@ size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits) {
 
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits) {
   const size_t q = static_cast<size_t>(Q), s = static_cast<size_t>(splits);
-  const size_t cap = static_cast<size_t>(candidate_cap(K));
+  const size_t cap = static_cast<size_t>(decode_candidate_cap(K));
   char* b = static_cast<char*>(base);
   DecodeScratch w;
   auto take = [&](size_t bytes) {
@@ -563,7 +563,7 @@ hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t spli
   a.Q = static_cast<int32_t>(p.Q);
   a.splits = splits;
   a.w = w;
-  a.cap = candidate_cap(p.K);
+  a.cap = decode_candidate_cap(p.K);
   a.no_fallback = no_fallback ? 1 : 0;
   if (p.K == 512) launch_decode_k<512>(a, p, mode, status, st, mark);
   else launch_decode_k<1024>(a, p, mode, status, st, mark);

@@ -147,12 +147,14 @@ struct Geometry<1024> {
 constexpr int kPoolCap = 1856;
 constexpr int kFallbackGrid = 256;
 
-// The calibration samples every 32nd position: half the scoring work of a
-// 1/16 sample, and the looser gate (about 32 k' keys pass it) still fits the
-// candidate buffer. Measured at Q = 8192, C4 = 196,608, K = 1024: calibration
-// 0.65 -> 0.37 ms, call 8.45 -> 8.22 ms; with a 2,560-key buffer the same stride
-// overflowed rows into the exact fallback and took 10.4 ms.
-constexpr int kCalStride = 32;
+// The calibration samples every 64th position: a quarter of a 1/16 sample's
+// scoring work. The looser gate (about 64 k' keys pass it) needs the larger
+// candidate buffer (candidate_cap). Measured at Q = 8192, C4 = 196,608, K = 1024
+// (same session, outputs identical): 1/32 sample with a 4,096-key buffer,
+// calibration 0.33 ms, call 8.24 ms; 1/64 with 5,120 keys, 0.185 ms, scan +0.06
+// and merge +0.02 ms, call 8.17 ms; 1/64 with 4,096 keys overflowed rows into the
+// exact fallback (call 9.28 ms).
+constexpr int kCalStride = 64;
 constexpr int kCalPerPage = kPage / kCalStride;   // sampled positions per page
 static_assert(kCalStride >= 16 && kCalStride <= kPage && kPage % kCalStride == 0, "stride divides the page");
 constexpr int kCalCap = 512;         // calibration pool per row
@@ -164,7 +166,7 @@ constexpr int kCalMaxSplits = 8;
 constexpr int kCalMinSplitBlocks = 4;   // fewer sample blocks per split: the combine launch costs more than it saves
 constexpr int kCalListCap = 128;
 constexpr int kCalHeaders = kCalMaxSplits * kCalListCap;   // header words start here
-static_assert(kCalHeaders + kCalMaxSplits <= 3072, "split lists fit the smallest candidate buffer");
+static_assert(kCalHeaders + kCalMaxSplits <= candidate_cap(512), "split lists fit the smallest candidate buffer");
 
 // Score blocks [a, a+n) visited by a CTA.
 struct BlockSeq {
@@ -251,57 +253,68 @@ struct BlockDma {
   }
 };
 
-// "Sample blocks" of the calibration: sample block v holds the positions
-// base + kCalStride * (256 v + p), p = 0..255 (base = first position of the row
-// tile's range, a multiple of 256), i.e. every 32nd position, two per page. Same LDS
-// image as a score block (position p at slot p, same chunk swizzle), so the
-// block scorer applies unchanged. Every lane copies from its own page.
+// "Sample blocks" of the calibration. The calibration samples every
+// kCalStride-th position of the row tile's range: J = (u1 - u0) * kTile /
+// kCalStride samples, sample j at position base + kCalStride * j (base = first
+// position of the range, a multiple of 256). Sample block v (0 <= v < nb =
+// ceil(J / 256)) holds samples j = v + nb * p, p = 0..255: each block is spread
+// over the whole range, so the samples a row has seen after a few blocks are an
+// even subset of its whole sample, which the calibration's early compaction
+// relies on (and which keeps rows whose order is decided by index away from the
+// fallback). Same LDS image as a score block (sample p at slot p, same chunk
+// swizzle), so the block scorer applies unchanged. Every lane copies from its
+// own page.
 struct SampleDma {
   int base_pg;   // first logical page of the sampled range
-  int run;       // first block position of the wave's 32
+  int nb;        // sample blocks of the range
+  int run;       // first block slot of the wave's 32
 
-  __device__ __forceinline__ void init(int u0, int w, int) {
+  __device__ __forceinline__ void init(int u0, int blocks, int w) {
     base_pg = u0 * kTilePages;
+    nb = blocks;
     run = 32 * w;
   }
 
-  // Per-lane source layout, recomputed at every use from a lane index the
-  // compiler cannot hoist (an opaque copy): the loop-invariant 64-bit per-lane
-  // addresses it would otherwise keep for the whole scan do not fit the
-  // 128-VGPR budget of four waves per SIMD.
+  // Per-lane source layout of block v, recomputed at every use from a lane index
+  // the compiler cannot hoist (an opaque copy): loop-invariant 64-bit per-lane
+  // addresses kept for the whole calibration do not fit the 128-VGPR budget of
+  // four waves per SIMD.
   struct Lane {
-    int pg0, pg1, pg_sc;      // page index inside a sample block
-    int off0, off1, off_sc;   // byte offset inside the source page
+    int j0, j1, js;           // sample indices of the lane's two code chunks and its scale
+    int off0, off1, off_sc;   // byte offsets inside their source pages
   };
-  __device__ __forceinline__ Lane lane_layout() const {
+  __device__ __forceinline__ Lane lane_layout(int v) const {
     int lane;
     __asm__ __volatile__("v_and_b32 %0, 63, %1" : "=v"(lane) : "v"(static_cast<int>(threadIdx.x)));
     const int pq = lane >> 2, slot = lane & 3;
     const int p0 = run + pq, p1 = p0 + 16, ps = run + (lane & 31);
-    return Lane{p0 / kCalPerPage, p1 / kCalPerPage, ps / kCalPerPage,
-                kCalStride * (p0 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p0)),
-                kCalStride * (p1 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p1)),
-                kCalStride * (ps % kCalPerPage) * kVecScales};
+    const int j0 = v + nb * p0, j1 = v + nb * p1, js = v + nb * ps;
+    return Lane{j0, j1, js,
+                kCalStride * (j0 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p0)),
+                kCalStride * (j1 % kCalPerPage) * kVecBytes + 16 * (slot ^ chunk_swizzle(p1)),
+                kCalStride * (js % kCalPerPage) * kVecScales};
   }
 
   struct Ent {
     int32_t e0, e1, es;
+    int v;   // the block (wave-uniform)
   };
   // Uniform base + 32-bit unsigned byte offset (lp < 2^25), so the load uses a
-  // scalar base and one offset VGPR per entry.
+  // scalar base and one offset VGPR per entry. Entries beyond the table (samples
+  // past the range's end) are -1: nothing is copied for them.
   __device__ __forceinline__ static int32_t entry(const ScanArgs& a, int lp) {
     const uint32_t off = static_cast<uint32_t>(lp) * 4u;
     return lp < a.P_log ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(a.page_table) + off) : -1;
   }
   __device__ __forceinline__ Ent entries(const ScanArgs& a, int v, int) const {
-    const Lane l = lane_layout();
-    const int b = base_pg + v * (kTile / kCalPerPage);   // sample block v spans kTile / kCalPerPage pages
-    return Ent{entry(a, b + l.pg0), entry(a, b + l.pg1), entry(a, b + l.pg_sc)};
+    const Lane l = lane_layout(v);
+    return Ent{entry(a, base_pg + l.j0 / kCalPerPage), entry(a, base_pg + l.j1 / kCalPerPage),
+               entry(a, base_pg + l.js / kCalPerPage), v};
   }
 
   __device__ __forceinline__ void issue(const ScanArgs& a, const Ent& e, uint8_t* codes, uint8_t* scales,
                                         int lane) const {
-    const Lane l = lane_layout();
+    const Lane l = lane_layout(e.v);
     if (e.e0 >= 0 && e.e0 < a.P_phys)
       __builtin_amdgcn_global_load_lds(a.k_pages + static_cast<size_t>(e.e0) * (kPage * kVecBytes) + l.off0,
                                        codes + run * kVecBytes, 16, 0, 0);
@@ -313,6 +326,26 @@ struct SampleDma {
                                        scales + run * kVecScales, 4, 0, 0);
   }
 };
+
+// Samples j in [lo, hi) with va <= j mod nb < vb: the samples of blocks [va, vb)
+// inside a row's sample range.
+__device__ __forceinline__ int samples_in_blocks(int lo, int hi, int nb, int va, int vb) {
+  auto f = [&](int x) { return (x / nb) * (vb - va) + min(max(x % nb - va, 0), vb - va); };
+  return hi > lo ? f(hi) - f(lo) : 0;
+}
+
+// Keys the calibration pool keeps when it fills before the end of the row's
+// sample: having seen `seen` of its m samples (an even subset, see SampleDma),
+// the number of the sample's final top-k' among them is about Binomial(seen,
+// k'/m) with mean mu; keeping the top mu + 6 sqrt(mu) + 6 (at most k') of what
+// was seen loses none of the final top-k' except with probability below 1e-8,
+// and the gate raised to the kept ones' smallest key lets few later keys in, so
+// the pool rarely fills again. (Should it lose one, the row's final gate is a
+// smaller key: a superset of candidates, still exact.)
+__device__ __forceinline__ int provisional_keep(int kp, int seen, int m) {
+  const float mu = static_cast<float>(kp) * static_cast<float>(seen) / static_cast<float>(max(m, 1));
+  return min(kp, static_cast<int>(ceilf(mu + 6.0f * sqrtf(mu) + 6.0f)));
+}
 
 // One step of the stream: start the copy of block i+1 into the other buffer,
 // score block i, then wait for the copy and for every wave.
@@ -493,27 +526,35 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
   uint64_t gate = 0;
   bool bad = false;
   if (mode == 0) {
+    const int nb = ((u1 - u0) * (kTile / kCalStride) + kTile - 1) / kTile;   // sample blocks
+    const BlockSeq seq = split_range(0, nb, static_cast<int>(blockIdx.y), static_cast<int>(gridDim.y));
+    // this split's samples inside the row's window (all of them when unsplit)
+    const int m_here = gated ? samples_in_blocks(j_lo, j_hi, nb, seq.a, seq.a + seq.n) : 0;
     SampleDma d;
-    d.init(u0, wave, lane);
+    d.init(u0, nb, wave);
     const LaneOffsets lo = lane_offsets(lane);
-    const BlockSeq seq = split_range(0, (u1 - u0 + kCalStride - 1) / kCalStride, static_cast<int>(blockIdx.y),
-                                     static_cast<int>(gridDim.y));
+    int seen = 0;   // samples of the row's window scored so far (wave-uniform)
     stream_dma(a, d, seq, s_codes0, s_scales0, s_codes1, s_scales1,
                [&](int v, const uint8_t* codes, const uint8_t* scales) {
       if (!gated) return;
-      const int vb = base + kCalStride * kTile * v;   // position of sample 0 of block v
-      if (vb >= end || vb + kCalStride * kTile <= start) return;
       score_block(qr, codes, scales, lo, [&](int blk, float sc) {
-        const int pos = vb + kCalStride * (64 * blk + lane);
+        // from a lane index the compiler cannot hoist: a per-lane multiple of nb kept
+        // for the whole calibration would push it past 128 VGPRs
+        int ln;
+        __asm__ __volatile__("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"(static_cast<int>(threadIdx.x)));
+        const int pos = base + kCalStride * (v + nb * (64 * blk + ln));
+        const bool in_win = pos >= start && pos < end;
+        seen += __popcll(__ballot(in_win));
         const uint64_t key = make_key(sc, static_cast<uint32_t>(pos));
-        bool pass = pos >= start && pos < end && key > gate;
+        bool pass = in_win && key > gate;
         uint64_t msk = __ballot(pass);
         if (msk == 0) return;
         int cnt = __popcll(msk);
         if (fill + cnt > kCalCap) {
-          const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
-          if (sel.kept != kp) bad = true;
-          fill = kp;
+          const int keep = min(provisional_keep(kp, seen, m_here), fill - 1);
+          const Selected sel = wave_select_compact(pool, fill, keep, s_hist[wave], lane);
+          if (sel.kept != keep) bad = true;
+          fill = keep;
           gate = sel.T - 1;
           pass = pass && key > gate;
           msk = __ballot(pass);
@@ -555,13 +596,15 @@ __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandA
   } else if (mode == 2) {
     row_gate = ~0ull;                                 // nothing passes: underfill
   } else if (gated) {
-    uint64_t T;
+    uint64_t T = 0;
     if (fill > kp) {
       const Selected sel = wave_select_compact(pool, fill, kp, s_hist[wave], lane);
       if (sel.kept != kp) bad = true;
       T = sel.T;
-    } else {
+    } else if (fill == kp) {
       T = wave_min_key(pool, fill, lane);
+    } else {
+      bad = true;   // an early compaction kept too few keys (probability < 1e-8): exact fallback
     }
     row_gate = T - 1;
     if (bad) {                                        // selector failure: exact fallback
@@ -1013,7 +1056,7 @@ __global__ void __launch_bounds__(1024, 8) logits_topk_kernel(
     int32_t* __restrict__ out_slot, int32_t* __restrict__ out_count, float* __restrict__ out_score) {
   constexpr int NT = 1024;
   constexpr int E = kSelChunks * kSelChunk / NT;   // sample keys per thread
-  constexpr int CAP = candidate_cap(K);
+  constexpr int CAP = selector_candidate_cap(K);
   __shared__ uint64_t s_cand[CAP];
   __shared__ uint64_t s_sel[K];
   __shared__ uint32_t s_hist[2048];

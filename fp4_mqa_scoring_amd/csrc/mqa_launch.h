@@ -41,12 +41,17 @@ struct GatedScratch {
   uint64_t* cand;       // [Q, candidate_cap(K)]
 };
 
-// Candidate keys kept per row by the gated paths. A gate from the k'-th key of
-// a 1/32 position sample passes about 32 k' keys with a spread of about
-// 32 sqrt(k'): 2,016 +- 254 at K = 1024 (k' = 63) and 1,280 +- 202 at K = 512
-// (k' = 40), so 4,096 and 3,072 leave more than 8 sigma before a row overflows
-// into the exact fallback.
-constexpr int candidate_cap(int K) { return K == 512 ? 3072 : 4096; }
+// Candidate keys kept per row by the fused path's gated scan. The gate is the
+// k'-th key of a 1/64 position sample (k' = x + 4 sqrt(x) + 8, x = K m / n: 40
+// at K = 1024, 28 at K = 512); the keys above it number k' + NegBinomial(k',
+// 1/64): 2,560 +- 405 and 1,792 +- 339. 5,120 and 4,096 keys make an overflow
+// (the row then takes the exact fallback) rarer than 1e-6 per row.
+constexpr int candidate_cap(int K) { return K == 512 ? 4096 : 5120; }
+// The decode path's gate samples every 32nd page (about 2,016 +- 254 and 1,280
+// +- 202 keys pass it), and the dense selector's samples 128 chunks of 64
+// logits: both keep the smaller buffers.
+constexpr int decode_candidate_cap(int K) { return K == 512 ? 3072 : 4096; }
+constexpr int selector_candidate_cap(int K) { return K == 512 ? 3072 : 4096; }
 
 // Keys a row's pool holds in the context-tiled path (K after each compaction,
 // appended tile keys above its floor up to this many).
@@ -71,7 +76,7 @@ struct DecodeScratch {
   uint64_t* keys;       // [Q, splits, K]   fallback: top-K per (row, split)
   uint64_t* gate;       // [Q]
   uint32_t* cand_n;     // [Q]              candidates appended (may exceed cap: overflow)
-  uint64_t* cand;       // [Q, candidate_cap(K)]
+  uint64_t* cand;       // [Q, decode_candidate_cap(K)]
   int32_t* fb_list;     // [Q]              rows sent to the fallback
   int32_t* fb_count;    // [1]              (cleared by row_prep)
 };

@@ -153,7 +153,7 @@ int32_t mqa_fp4_topk_prefill_ex(const uint8_t* q, const uint8_t* q_scale, int64_
  * scratch -- mqa_fp4_topk_scratch_bytes(num_rows, K, device) bytes -- comes
  * from a fixed array of MQA_STATIC_SCRATCH_BYTES bytes that the library keeps
  * on every device it runs on until the process ends, so num_rows is limited to
- * what fits: 2,045 rows at K = 1024 and 2,726 at K = 512; a larger batch
+ * what fits: 1,636 rows at K = 1024 and 2,045 at K = 512; a larger batch
  * returns MQA_ERR_BAD_SIZE with nothing launched. The call allocates and frees
  * nothing, never synchronises, and accepts a capturing stream (the kernels
  * write every scratch word before reading it, so replays need no clearing).

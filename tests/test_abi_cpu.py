@@ -193,7 +193,7 @@ def test_decode_entry_checks_arguments_on_host(lib):
 
 def test_allocation_free_entry_point_checks_its_limit_on_host(lib):
     """The allocation-free prefill form takes its scratch from a fixed 64 MiB
-    per-device array: 2,045 rows fit at K = 1024 and 2,726 at K = 512, one more
+    per-device array: 1,636 rows fit at K = 1024 and 2,045 at K = 512, one more
     is rejected with MQA_ERR_BAD_SIZE before any HIP call."""
     import fp4_mqa_scoring_amd as m
     assert m.STATIC_SCRATCH_BYTES == 64 << 20
@@ -201,9 +201,9 @@ def test_allocation_free_entry_point_checks_its_limit_on_host(lib):
 
     def call(Q, K, flags=0):
         return lib.mqa_fp4_topk_prefill_static(p, p, Q, p, p, 2, p, p, 2, p, p, K, p, p, p, None, flags, None)
-    assert call(2046, 1024) == -4
-    assert call(2727, 512) == -4
-    assert call(2045, 1024) != -4                   # fits: fails later, at the device checks (no GPU here)
-    assert call(2726, 512) != -4
+    assert call(1637, 1024) == -4
+    assert call(2046, 512) == -4
+    assert call(1636, 1024) != -4                   # fits: fails later, at the device checks (no GPU here)
+    assert call(2045, 512) != -4
     assert call(10, 700) == -1
     assert call(10, 512, flags=0x500) == -8

@@ -54,18 +54,18 @@ def _inputs(Q, S, K, seed):
 
 
 def test_two_calls_in_a_row_match_the_allocating_entry_point():
-    """A 2,045-row batch (the limit at K = 1024) then a smaller one at K = 512,
+    """A 1,636-row batch (the limit at K = 1024) then a smaller one at K = 512,
     then the first again: each equals mqa_fp4_topk_prefill_ex bit for bit."""
     _need_gpu()
-    big = _inputs(2045, 64 * 300, 1024, 11)
+    big = _inputs(1636, 64 * 300, 1024, 11)
     small = _inputs(37, 64 * 90, 512, 12)
     db, ds = gu.to_device(big), gu.to_device(small)
     want_big = _run(db, 1024, static=False)
     want_small = _run(ds, 512, static=False)
     mqa.mqa_fp4_status()
-    _same(want_big, _run(db, 1024, static=True), "first call, 2,045 rows")
+    _same(want_big, _run(db, 1024, static=True), "first call, 1,636 rows")
     _same(want_small, _run(ds, 512, static=True), "second call, 37 rows")
-    _same(want_big, _run(db, 1024, static=True), "third call, 2,045 rows again")
+    _same(want_big, _run(db, 1024, static=True), "third call, 1,636 rows again")
     assert mqa.mqa_fp4_status() == mqa.STATUS_BAD_WINDOW | mqa.STATUS_BAD_PAGE
 
 
@@ -82,7 +82,7 @@ def test_flags_match_the_allocating_entry_point(flags):
 def test_batches_beyond_the_array_are_rejected_and_write_nothing():
     _need_gpu()
     import torch
-    inp = _inputs(2046, 64 * 40, 1024, 14)
+    inp = _inputs(1637, 64 * 40, 1024, 14)
     dev = gu.to_device(inp)
     outs = mqa.alloc_outputs(inp.Q, 1024, "cuda")
     for t in outs:
