@@ -58,7 +58,11 @@ def code_hash(*files: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    return code_hash("mqa_device.h", "mqa_select.h", "mqa_kernels.hip")
+    return code_hash("mqa_device.h", "mqa_select.h", "mqa_launch.h", "mqa_kernels.hip")
+
+
+def decode_source_hash() -> str:
+    return code_hash("mqa_device.h", "mqa_select.h", "mqa_launch.h", "mqa_decode.hip")
 
 
 class HipEvents:
@@ -287,7 +291,7 @@ def bench_decode(args, torch, mqa, dev):
     if os.path.exists(tf):
         with open(tf) as fh:
             tr = json.load(fh)
-        if tr.get("kernel_source_hash") == code_hash("mqa_device.h", "mqa_select.h", "mqa_decode.hip"):
+        if tr.get("kernel_source_hash") == decode_source_hash():
             traffic = tr.get("bytes_per_launch")
     line = {
         "metric": "ms/call + scored pairs/s, decode batch (multi-sequence form, HIP graph replay)",

@@ -609,7 +609,7 @@ int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t nu
   rc = hip_rc(mqa::launch_row_prep(p, 0, w.row_state, w.fb_count, st));
   record_stage(1, st);
   if (rc == MQA_OK)
-    rc = hip_rc(mqa::launch_decode(p, w, sp, mode, (flags & MQA_FLAG_NO_FALLBACK) != 0, st,
+    rc = hip_rc(mqa::launch_decode(p, w, sp, mode, (flags & MQA_FLAG_NO_FALLBACK) != 0, info.cus, st,
                                    t_stage_events ? record_stage : nullptr));
   record_stage(4, st);
   return rc;

@@ -79,7 +79,18 @@ struct DecodeScratch {
   uint64_t* cand;       // [Q, decode_candidate_cap(K)]
   int32_t* fb_list;     // [Q]              rows sent to the fallback
   int32_t* fb_count;    // [1]              (cleared by row_prep)
+  int64_t* plan;        // [Q + 1]          gated scan: pages of the rows before each row
+  uint64_t* wave_keys;  // [kDecScanWaves, kDecWaveStride] gated scan: each wave's candidates
+  uint32_t* wave_first; // [kDecScanWaves]  candidates of the wave's first segment
+  uint32_t* row_off;    // [Q]              where the row's first segment's candidates start
+  uint32_t* row_first;  // [Q]              and how many there are
+  uint32_t* row_w0;     // [Q]              first scan wave over the row's pages
+  uint32_t* row_nw;     // [Q]              and the number of waves
+  int64_t* wave_desc;   // [kDecScanWaves, 3] a scan wave's pages [g0, g1) and its first row
 };
+constexpr int kDecScanWaves = 3072;   // gated scan waves at most (three 4-wave blocks per CU on 256 CUs)
+constexpr int kDecWaveKeys = 512;     // candidate keys a scan wave keeps before spilling to the row's buffer
+constexpr int kDecWaveStride = kDecWaveKeys + 16;   // and a 128-byte line its lanes without a key write to
 constexpr int kMaxDecodeSplits = 64;
 size_t decode_scratch_bytes(int64_t Q, int32_t K, int32_t splits);
 DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t splits);
@@ -87,8 +98,10 @@ DecodeScratch decode_scratch_layout(void* base, int64_t Q, int32_t K, int32_t sp
 typedef void (*StageMark)(int, hipStream_t);
 // mode 0 gated, 1 no prefilter (every long row takes the exact fallback), 2 forced underfill;
 // no_fallback: rows the gated pass cannot finish fail closed instead (as for the prefill path).
+// The gated scan runs on a fixed grid for `cus` compute units; `splits` is the
+// fallback's context splits per row.
 hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t splits, int mode, bool no_fallback,
-                         hipStream_t st, StageMark mark = nullptr);
+                         int cus, hipStream_t st, StageMark mark = nullptr);
 
 // Bounded context-tiled exact TopK over long rows (row_state from row_prep):
 // tile_logits [Q, tile] fp32, running [Q, K] keys and run_count [Q] are scratch.

@@ -276,21 +276,28 @@ int32_t mqa_fp4_set_stage_events(void* const* events, int32_t n);
  *                                             [0, num_seqs) fails with code -1
  *   workspace   device memory of at least mqa_fp4_decode_workspace_bytes(Q, K,
  *               splits, device) bytes, 256-byte aligned, owned by the caller;
- *               its contents need no initialisation and are scratch only
- *   splits      context splits per row (1..64), 0 = automatic for the device
+ *               its contents need no initialisation and are scratch only (the
+ *               size is O(Q * splits * K) plus a fixed 12.5 MiB for the gated
+ *               scan's per-wave candidate regions, independent of the context)
+ *   splits      context splits per row of the exact fallback (1..64), 0 =
+ *               automatic for the device
  * The call allocates nothing, never synchronises and accepts a capturing
  * stream; row failures are reported in out_count and the sticky status word
  * only (read mqa_fp4_status outside the graph). Each row is scanned
  * independently (no key sharing between rows): a calibrated gate per row from
  * every 32nd page (PR 5309's calibrated candidate filter; a coarser multiple of
- * 32 on windows beyond 262,144 positions), then one wave per (row, split) for a
- * gated scan into a bounded per-row candidate buffer and an exact merge; rows
- * that underfill or overflow are recomputed exactly by per-wave bounded LDS
- * pools (PR 5282's streaming design) with an exact merge of the splits. flags:
- * MQA_FLAG_NO_PREFILTER or MQA_FLAG_FORCE_UNDERFILL (for tests; the split bits
- * must be 0, splits are the separate argument). Outputs do not depend on the
- * splits or the flags. Two calls that share a workspace must be ordered (same
- * stream).
+ * 32 on windows beyond 262,144 positions), then a gated scan in which the
+ * device's waves share all rows' pages evenly (each wave's share within one row
+ * when rows are few), each keeping its candidates in a region of its own, and
+ * an exact merge per row; rows that underfill or overflow are recomputed
+ * exactly by per-wave bounded LDS pools (PR 5282's streaming design) with an
+ * exact merge of the splits. flags: MQA_FLAG_NO_PREFILTER or
+ * MQA_FLAG_FORCE_UNDERFILL (for tests), MQA_FLAG_NO_FALLBACK (fail closed
+ * instead of the fallback, as for mqa_fp4_topk_prefill_ex; not with
+ * MQA_FLAG_NO_PREFILTER); the split bits must be 0, splits are the separate
+ * argument. Outputs do not depend on the splits or the flags (except rows that
+ * MQA_FLAG_NO_FALLBACK fails closed). Two calls that share a workspace must be
+ * ordered (same stream).
  */
 int32_t mqa_fp4_topk_decode(const uint8_t* q, const uint8_t* q_scale, int64_t num_rows, const uint8_t* k_pages,
                             const uint8_t* k_scale, int64_t num_phys_pages, const float* weights,

@@ -182,12 +182,14 @@ def test_decode_entry_checks_arguments_on_host(lib):
     assert call(ws_bytes=-1) == -4
     assert call(ws=None) == -2
     assert call(ws=P(0x1010)) == -3                  # workspace needs 256-byte alignment
-    # explicit splits: no device query; O(Q) + Q*splits*(4 + 8K) bytes
+    # explicit splits: no device query; O(Q) + Q*splits*(4 + 8K) bytes, the scan plan (Q + 1) * 8, and the
+    # gated scan's per-wave candidate regions (3072 waves x (512 + 16) keys), counts and descriptors
     q, K, s = 100, 1024, 5
     a = lambda x: (x + 255) // 256 * 256
     cap = 4096                                       # candidate keys per row at K = 1024
+    waves = 3072
     want = (a(q * 4) + a(q * s * 4) + a(q * s * K * 8) + a(q * 8) + a(q * 4) + a(q * cap * 8) + a(q * 4)
-            + a(4))
+            + a(4) + a((q + 1) * 8) + a(waves * 528 * 8) + a(waves * 4) + 4 * a(q * 4) + a(waves * 3 * 8))
     assert m.mqa_fp4_decode_workspace_bytes(q, K, s) == want
 
 

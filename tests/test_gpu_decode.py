@@ -190,6 +190,36 @@ def test_decode_shape_long_contexts_sampled_rows():
     assert np.all(res[2] == np.minimum(n, 1024))
 
 
+def test_scan_shares_span_many_rows():
+    """20,000 rows of 400..720 positions at K = 512: more rows than the gated
+    scan has waves, so each wave's equal share of all rows' pages runs over
+    several rows, with short rows (no pages to scan) and rows of an invalid
+    sequence between them. Bit-equal to the no-prefilter run (the exact fallback,
+    which splits every row the same way) on every row; sampled rows against the
+    oracle."""
+    _need_gpu()
+    K = 512
+    d = synth.make_decode_inputs(5000, 4, 400, 720, K, seed=4242)
+    for r in (3, 4, 5, 777, 19999):
+        d.seq_of_row[r] = 5000 + r                            # invalid sequence: code -1
+    t = _dev(d)
+    mqa.mqa_fp4_status()
+    base = run_decode(t, K)
+    assert mqa.mqa_fp4_status() == mqa.STATUS_BAD_WINDOW
+    n = d.lengths()
+    bad = np.zeros(d.Q, bool)
+    bad[[3, 4, 5, 777, 19999]] = True
+    assert np.all(base[2][bad] == -1)
+    assert np.all(base[2][~bad] == np.minimum(n[~bad], K))
+    assert (n[~bad] <= K).sum() > 1000 and (n[~bad] > K).sum() > 10000
+    got = run_decode(t, K, flags=mqa.FLAG_NO_PREFILTER)
+    assert mqa.mqa_fp4_status() == mqa.STATUS_BAD_WINDOW     # read and cleared
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rows = [r for r in np.random.default_rng(7).choice(d.Q, 48, replace=False) if not bad[r]]
+    check_decode(d, base, rows=rows + [0, 1, 2, 6, 19998], where="shares over many rows")
+
+
 @pytest.mark.parametrize("K", [512, 1024])
 def test_windows_beyond_the_sample_budget(K):
     """Windows of 140,000..300,000 positions (2,188..4,688 pages): the per-row
