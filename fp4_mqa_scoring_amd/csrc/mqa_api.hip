@@ -142,6 +142,21 @@ int32_t auto_splits(int64_t Q, int cus, int per_cu = 2) {
   return static_cast<int32_t>(s);
 }
 
+// Context splits of the gated scan: as auto_splits, and at least
+// min(8, blocks / 64) for a context of `blocks` 256-position blocks. Shorter
+// CTAs end the launch more evenly: at Q = 8192, C4 = 196,608 (1,024 row tiles,
+// one split by the CU count alone) 1 / 2 / 4 / 8 / 16 splits took 7.50 / 7.38 /
+// 7.32 / 7.32 / 7.32 ms (scan kernel, same session), outputs identical; the
+// calibration keeps auto_splits (its combine launch costs more than it saves
+// once the row tiles fill the CUs).
+int32_t scan_splits(int64_t Q, int64_t P_log, int cus) {
+  const int64_t blocks = (P_log * 64 + 255) / 256;
+  int64_t floor_s = blocks / 64;
+  if (floor_s > 8) floor_s = 8;
+  const int32_t s = auto_splits(Q, cus, 4);
+  return static_cast<int32_t>(floor_s > s ? floor_s : s);
+}
+
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 constexpr int32_t kDefaultTile = 4096;   // positions per tile of the context-tiled path
@@ -269,8 +284,9 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st, bool use_st
   rc = enter(st, specs, sizeof(specs) / sizeof(specs[0]), guard, &info, /*allow_capture=*/use_static);
   if (rc != MQA_OK) return rc;
   if (!rows) return MQA_OK;
-  const int32_t splits = (flags & MQA_FLAG_SPLITS_MASK) ? static_cast<int32_t>(flags & MQA_FLAG_SPLITS_MASK)
-                                                        : auto_splits(p.Q, info.cus, 4);
+  const int32_t explicit_splits = static_cast<int32_t>(flags & MQA_FLAG_SPLITS_MASK);
+  const int32_t splits = explicit_splits ? explicit_splits : scan_splits(p.Q, p.P_log, info.cus);
+  const int32_t calib_splits = explicit_splits ? explicit_splits : auto_splits(p.Q, info.cus, 4);
   const int calib_mode = (flags & MQA_FLAG_NO_PREFILTER) ? 1 : (flags & MQA_FLAG_FORCE_UNDERFILL) ? 2 : 0;
   Scratch allocated;
   char* base = nullptr;
@@ -298,7 +314,8 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st, bool use_st
   rc = hip_rc(mqa::launch_row_prep(p, 0, g.row_state, g.fb_count, st));
   record_stage(1, st);
   for (int stage = 0; stage < 5 && rc == MQA_OK; ++stage) {
-    rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_mode, (flags & MQA_FLAG_NO_FALLBACK) != 0, stage, st));
+    rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_splits, calib_mode, (flags & MQA_FLAG_NO_FALLBACK) != 0,
+                                        stage, st));
     if (stage <= 1) record_stage(2 + stage, st);   // after calibration, after the scan
   }
   record_stage(4, st);

@@ -1409,8 +1409,8 @@ hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int3
 }
 
 template <int K>
-static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
-                                 bool no_fallback, int stage, hipStream_t st) {
+static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
+                                 int calib_mode, bool no_fallback, int stage, hipStream_t st) {
   using G = Geometry<K>;
   const ScanArgs a = scan_args(p, g.row_state, splits);
   const CandArgs c = cand_args(g, K, no_fallback);
@@ -1420,7 +1420,7 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
       // split the calibration over the context when the row tiles alone leave CUs
       // idle and every split still gets kCalMinSplitBlocks sample blocks
       const int64_t sample_blocks = (p.P_log * kPage + kCalStride * kTile - 1) / (kCalStride * kTile);
-      int64_t cs = calib_mode == 0 ? splits : 1;
+      int64_t cs = calib_mode == 0 ? calib_splits : 1;
       if (cs > kCalMaxSplits) cs = kCalMaxSplits;
       if (cs > sample_blocks / kCalMinSplitBlocks) cs = sample_blocks / kCalMinSplitBlocks;
       if (cs < 1) cs = 1;
@@ -1448,11 +1448,11 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
   return hipGetLastError();
 }
 
-hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int calib_mode,
-                              bool no_fallback, int stage, hipStream_t st) {
+hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
+                              int calib_mode, bool no_fallback, int stage, hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
-  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_mode, no_fallback, stage, st)
-                    : launch_gated_k<1024>(p, g, splits, calib_mode, no_fallback, stage, st);
+  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, st)
+                    : launch_gated_k<1024>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, st);
 }
 
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
