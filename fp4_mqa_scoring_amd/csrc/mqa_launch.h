@@ -62,8 +62,9 @@ constexpr int tile_pool_cap(int K) { return 2 * K; }
 hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int32_t* fb_count, hipStream_t st);
 // Stages of the gated fused path: 0 calibration (calib_mode 0 normal, 1 no
 // prefilter, 2 forced underfill; calib_splits context splits), 1 gated scan
-// (splits context splits), 2 merge, 3 fallback scan, 4 fallback merge. With no_fallback the merge fails closed the rows it would
-// list for the fallback (underfill -3, overflow -4) and the list stays empty.
+// (splits context splits), 2 merge, 3 fallback scan, 4 fallback merge. With
+// no_fallback the merge fails closed the rows it would list for the fallback
+// (underfill -3, overflow -4) and the list stays empty.
 hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
                               int calib_mode, bool no_fallback, int stage, hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
