@@ -99,24 +99,28 @@ __device__ __forceinline__ const int32_t* row_table(const DecArgs& a, int row) {
   return a.block_table + static_cast<size_t>(a.seq_of_row[row]) * a.max_pages;
 }
 
-// One page (64 positions) of the paged cache into the wave's LDS slot, in the
+// One page (64 positions) of the paged cache into a wave's LDS buffer, in the
 // score-block image (position p at p * 64, chunk c at slot c ^ chunk_swizzle(p));
 // the swizzle is applied on the source side because a lane's LDS destination is
-// fixed by its lane id. Out-of-range entries are not copied (row_prep failed
-// every row whose window touches them).
-__device__ __forceinline__ bool page_dma(const DecArgs& a, int32_t e, uint8_t* codes, uint8_t* scales, int lane) {
-  if (e < 0 || e >= a.P_phys) return false;
+// fixed by its lane id. Five vector memory operations, whatever the entry: an
+// entry outside the cache is replaced by page 0 (row_prep has already failed
+// every row whose window touches one; this only keeps the copy in bounds). The
+// key cache is read once per row, so its lines are fetched with the
+// non-temporal policy (kNonTemporal).
+constexpr int kNonTemporal = 2;   // NT bit of the gfx950 cache-policy operand
+
+__device__ __forceinline__ void copy_page(const DecArgs& a, int32_t e, uint8_t* codes, uint8_t* scales, int lane) {
+  e = (e >= 0 && e < a.P_phys) ? e : 0;
   const uint8_t* page = a.k_pages + static_cast<size_t>(e) * kPageBytes;
   const int pq = lane >> 2, slot = lane & 3;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int p = 16 * j + pq;
     __builtin_amdgcn_global_load_lds(page + p * kVecBytes + 16 * (slot ^ chunk_swizzle(p)), codes + 16 * j * kVecBytes,
-                                     16, 0, 0);
+                                     16, 0, kNonTemporal);
   }
   __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e) * kPageScaleBytes + lane * kVecScales, scales, 4,
-                                   0, 0);
-  return true;
+                                   0, kNonTemporal);
 }
 
 // fp32 scores of the 64 positions of one LDS page image: lane l, position l.
@@ -175,57 +179,13 @@ __device__ __forceinline__ float score_page_asm(const QRow& qr, const uint8_t* c
   return combine_halves(h0, h1);
 }
 
-// The wave's LDS for the gate and fallback kernels: two page buffers as
-// separate variables (the loop below is unrolled by two). The table entries
-// come 64 at a time with the next chunk prefetched; the compiler waits for
-// those loads, and with them (vector memory operations retire in issue order)
-// for the copy in flight, before the current page's LDS reads, so here a page's
-// copy overlaps the other waves' work, not the wave's own scoring (the gated
-// scan's stream_pages3 avoids both waits).
+// The gate and fallback kernels' LDS: two page buffers per wave.
 struct WavePages {
   uint8_t* c0;
   uint8_t* s0;
   uint8_t* c1;
   uint8_t* s1;
 };
-
-// Streams pages first, first + stride, ... (< end_pg) of `table` through the
-// wave's two buffers and calls body(page, codes, scales) for each. Table entries
-// come 64 pages per vector load, the next chunk prefetched.
-template <class Body>
-__device__ __forceinline__ void stream_pages(const DecArgs& a, const int32_t* table, int first, int end_pg,
-                                             int stride, const WavePages& b, int lane, Body&& body) {
-  if (first >= end_pg) return;
-  const int n = (end_pg - first + stride - 1) / stride;
-  auto chunk = [&](int c) -> int32_t {
-    const int i = 64 * c + lane;
-    return i < n ? table[first + stride * i] : -1;
-  };
-  int32_t cur = chunk(0), nxt = chunk(1);
-  int base = 0;   // first stream index of chunk `cur`
-  auto entry = [&](int j) -> int32_t {   // stream index base + j, j < 128
-    return (j >> 6) == 0 ? __builtin_amdgcn_readlane(cur, j & 63) : __builtin_amdgcn_readlane(nxt, j & 63);
-  };
-  auto step = [&](int i, const uint8_t* codes, const uint8_t* scales, uint8_t* nc, uint8_t* ns) {
-    if (i + 1 < n) {
-      page_dma(a, entry(i + 1 - base), nc, ns, lane);
-      if (((i + 1 - base) >> 6) != 0) {   // page i + 1 opened the next chunk
-        cur = nxt;
-        base += 64;
-        nxt = chunk(base / 64 + 1);
-      }
-    }
-    body(first + stride * i, codes, scales);
-    vm_wait_all();
-  };
-  vm_wait_all();
-  page_dma(a, entry(0), b.c0, b.s0, lane);
-  vm_wait_all();
-  for (int i = 0; i < n; i += 2) {
-    step(i, b.c0, b.s0, b.c1, b.s1);
-    if (i + 1 < n) step(i + 1, b.c1, b.s1, b.c0, b.s0);
-  }
-}
 
 // Pages first .. end_pg - 1 of `table` through the wave's three buffers: while
 // one page is scored the next two are in flight. The table entries of each run
@@ -256,10 +216,8 @@ struct WavePages3 {
 // wait insertion takes into account, unlike a wait written in inline asm.
 constexpr int kWaitVm0 = 0x0F70;   // vmcnt(0)
 constexpr int kWaitVm5 = 0x0F75;   // vmcnt(5): all but the last page copy issued
-// Cache-policy operand of the page copies: the non-temporal bit (NT, bit 1 of
-// the gfx950 CPol field). Measured on a 64-row decode batch: the gated scan
-// 69 -> 63 us with identical outputs; the SC0 bit alone changed nothing.
-constexpr int kNonTemporal = 2;
+// (The non-temporal policy on the page copies: on a 64-row decode batch the gated
+// scan 69 -> 63 us with identical outputs; the SC0 bit alone changed nothing.)
 
 __device__ __forceinline__ void vm_wait_but_one_page() {
   __builtin_amdgcn_s_waitcnt(kWaitVm5);
@@ -278,22 +236,7 @@ __device__ __forceinline__ void stream_pages3(const DecArgs& a, const int32_t* t
     const int n = min(64, end_pg - run);
     const int32_t ent = lane < n ? table[run + lane] : -1;
     vm_wait_all_known();   // the entries
-    // copy of page i; the key cache is read once per row, so its lines are
-    // fetched with the non-temporal policy (kNonTemporal)
-    auto issue = [&](int i, uint8_t* c, uint8_t* sc) {
-      int32_t e = __builtin_amdgcn_readlane(ent, i);
-      e = (e >= 0 && e < a.P_phys) ? e : 0;
-      const uint8_t* page = a.k_pages + static_cast<size_t>(e) * kPageBytes;
-      const int pq = lane >> 2, slot = lane & 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = 16 * j + pq;
-        __builtin_amdgcn_global_load_lds(page + p * kVecBytes + 16 * (slot ^ chunk_swizzle(p)), c + 16 * j * kVecBytes,
-                                         16, 0, kNonTemporal);
-      }
-      __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e) * kPageScaleBytes + lane * kVecScales, sc, 4,
-                                       0, kNonTemporal);
-    };
+    auto issue = [&](int i, uint8_t* c, uint8_t* sc) { copy_page(a, __builtin_amdgcn_readlane(ent, i), c, sc, lane); };
     // page i in buffer (c, s), page i + 2 to buffer (fc, fs) if there is one
     auto step = [&](int i, const uint8_t* c, const uint8_t* sc, uint8_t* fc, uint8_t* fs) {
       const bool more = i + 2 < n;
@@ -313,6 +256,46 @@ __device__ __forceinline__ void stream_pages3(const DecArgs& a, const int32_t* t
       step(i, b.c0, b.s0, b.c2, b.s2);
       if (i + 1 < n) step(i + 1, b.c1, b.s1, b.c0, b.s0);
       if (i + 2 < n) step(i + 2, b.c2, b.s2, b.c1, b.s1);
+    }
+  }
+}
+
+// Pages first, first + stride, ... (< end_pg) of `table` through the wave's two
+// buffers, the gate's and the fallback's stream: while page i is scored the
+// copy of page i + 1 is in flight. Entries, reads and waits as in
+// stream_pages3: body reads its page with inline-asm LDS reads (which complete
+// before it returns, so the next copy may overwrite the buffer), and the waits
+// here order the reads after the copies.
+template <class Body>
+__device__ __forceinline__ void stream_pages2(const DecArgs& a, const int32_t* table, int first, int end_pg, int stride,
+                                              const WavePages& b, int lane, Body&& body) {
+  if (first >= end_pg) return;
+  const int total = (end_pg - first + stride - 1) / stride;
+  for (int run = 0; run < total; run += 64) {
+    const int n = min(64, total - run);
+    const int32_t ent = lane < n ? table[first + stride * (run + lane)] : -1;
+    vm_wait_all_known();   // the entries
+    auto issue = [&](int i, uint8_t* c, uint8_t* sc) { copy_page(a, __builtin_amdgcn_readlane(ent, i), c, sc, lane); };
+    // page i in buffer (c, s), then its buffer takes page i + 2 if there is one
+    auto step = [&](int i, uint8_t* c, uint8_t* sc) {
+      body(first + stride * (run + i), c, sc);
+      if (i + 2 < n) {
+        issue(i + 2, c, sc);
+        vm_wait_but_one_page();   // page i + 1 is in
+      } else {
+        vm_wait_all_known();
+      }
+    };
+    issue(0, b.c0, b.s0);
+    if (n > 1) {
+      issue(1, b.c1, b.s1);
+      vm_wait_but_one_page();
+    } else {
+      vm_wait_all_known();
+    }
+    for (int i = 0; i < n; i += 2) {
+      step(i, b.c0, b.s0);
+      if (i + 1 < n) step(i + 1, b.c1, b.s1);
     }
   }
 }
@@ -532,9 +515,11 @@ __global__ void __launch_bounds__(kDecGateWaves * 64) decode_gate_kernel(DecArgs
     return;
   }
   const int row = blockIdx.x - 1;
-  if (a.row_state[row] != kRowLong) return;
+  // the window is read beside the row's state rather than after it: one memory
+  // round trip less ahead of the page-table entries
+  const int state = a.row_state[row], start = a.row_start[row], end = a.row_end[row];
+  if (state != kRowLong) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int start = a.row_start[row], end = a.row_end[row];
   const int pg0 = start / kPage, pg1 = (end - 1) / kPage + 1;   // the window's pages [pg0, pg1)
   // L pages hold at most ceil(L / s) multiples of s: this stride leaves at most
   // B = 16 * kDecGateRegs sampled pages (kDecSampleStride up to that many times B pages).
@@ -560,10 +545,10 @@ __global__ void __launch_bounds__(kDecGateWaves * 64) decode_gate_kernel(DecArgs
 #pragma unroll
     for (int j = 0; j < kDecGateRegs; ++j) x[j] = 0ull;
     const int first = (pg0 + stride - 1) / stride * stride + stride * wave;
-    stream_pages(a, row_table(a, row), first, pg1, stride * kDecGateWaves,
+    stream_pages2(a, row_table(a, row), first, pg1, stride * kDecGateWaves,
                  WavePages{s_c0[wave], s_s0[wave], s_c1[wave], s_s1[wave]}, lane,
                  [&](int pg, const uint8_t* codes, const uint8_t* scales) {
-      const float sc = score_page(qr, codes, scales, lo);
+      const float sc = score_page_asm(qr, codes, scales, lo);
       const int pos = pg * kPage + lane;
       // shift register: the newest key enters at the top (static register names)
 #pragma unroll
@@ -843,9 +828,9 @@ __global__ void __launch_bounds__(kDecThreads, 2) decode_fb_scan_kernel(DecArgs 
     int fill = 0;
     uint64_t gate = 0;
     bool failed = false;
-    stream_pages(a, row_table(a, row), pa, pb, 1, WavePages{s_c0[wave], s_s0[wave], s_c1[wave], s_s1[wave]}, lane,
+    stream_pages2(a, row_table(a, row), pa, pb, 1, WavePages{s_c0[wave], s_s0[wave], s_c1[wave], s_s1[wave]}, lane,
                  [&](int pg, const uint8_t* codes, const uint8_t* scales) {
-      const float sc = score_page(qr, codes, scales, lo);
+      const float sc = score_page_asm(qr, codes, scales, lo);
       const int p0 = pg * kPage;
       const uint64_t win = (p0 >= start && p0 + kPage <= end) ? ~0ull : window_lanes(p0, start, end);
       const uint64_t key = make_key(sc, static_cast<uint32_t>(p0 + lane));

@@ -87,38 +87,82 @@ __device__ __forceinline__ void wave_lds_sync() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+// Cross-lane steps through DPP (gfx9 encodings), for code that runs with all 64
+// lanes active. dpp_take<CTRL, ROWS>(id, v) returns, in the rows set in ROWS, the
+// v of the lane that CTRL names, and `id` where that lane does not exist or the
+// row is not in ROWS: row_shr:n (0x110 + n) takes lane l - n of the same row of
+// 16, row_bcast:15 (0x142) lane 15 of the row before, row_bcast:31 (0x143)
+// lane 31.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_take(uint32_t id, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(id), static_cast<int>(v), CTRL, ROWS, 0xF, false));
 }
 
-__device__ __forceinline__ uint64_t wave_or64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v |= shfl_xor_u64(v, m);
+// Inclusive scan over lanes 0 .. this lane of an associative, commutative op
+// with identity id (Kogge-Stone inside each row of 16, then the row totals).
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_take<0x111, 0xF>(id, v));
+  v = op(v, dpp_take<0x112, 0xF>(id, v));
+  v = op(v, dpp_take<0x114, 0xF>(id, v));
+  v = op(v, dpp_take<0x118, 0xF>(id, v));
+  v = op(v, dpp_take<0x142, 0xA>(id, v));   // rows 1 and 3 take the row before
+  v = op(v, dpp_take<0x143, 0xC>(id, v));   // rows 2 and 3 take lanes 0 .. 31
   return v;
 }
 
-__device__ __forceinline__ uint64_t wave_and64(uint64_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v &= shfl_xor_u64(v, m);
-  return v;
+// Inclusive prefix sum over lanes (all lanes active).
+__device__ __forceinline__ uint32_t wave_prefix_sum_dpp(uint32_t v) {
+  return wave_scan_dpp(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
 }
 
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = max(v, __shfl_xor(v, m, 64));
-  return v;
+// Lane 63's value, zero-extended (readlane returns a signed int).
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
 }
 
-// Inclusive suffix sum over lanes: sum of v over lanes >= this lane.
-__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += t;
-  }
-  return v;
+// OR, AND and signed max of all 64 lanes, as a wave-uniform value (all lanes active).
+__device__ __forceinline__ uint64_t wave_all_or64(uint64_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return x | y; };
+  const uint32_t lo = wave_scan_dpp(static_cast<uint32_t>(v), 0u, op);
+  const uint32_t hi = wave_scan_dpp(static_cast<uint32_t>(v >> 32), 0u, op);
+  return (static_cast<uint64_t>(lane63(hi)) << 32) | lane63(lo);
+}
+
+__device__ __forceinline__ uint64_t wave_all_and64(uint64_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return x & y; };
+  const uint32_t lo = wave_scan_dpp(static_cast<uint32_t>(v), ~0u, op);
+  const uint32_t hi = wave_scan_dpp(static_cast<uint32_t>(v >> 32), ~0u, op);
+  return (static_cast<uint64_t>(lane63(hi)) << 32) | lane63(lo);
+}
+
+__device__ __forceinline__ int wave_all_max_i32(int v) {
+  const uint32_t m = wave_scan_dpp(static_cast<uint32_t>(v), static_cast<uint32_t>(INT_MIN),
+                                   [](uint32_t x, uint32_t y) {
+                                     return static_cast<uint32_t>(max(static_cast<int>(x), static_cast<int>(y)));
+                                   });
+  return __builtin_amdgcn_readlane(static_cast<int>(m), 63);
+}
+
+// One step of a 64-bit min over lanes: both halves of the neighbour's value move.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t min64_step(uint64_t v) {
+  const uint64_t y = (static_cast<uint64_t>(dpp_take<CTRL, ROWS>(~0u, static_cast<uint32_t>(v >> 32))) << 32) |
+                     dpp_take<CTRL, ROWS>(~0u, static_cast<uint32_t>(v));
+  return v < y ? v : y;
+}
+
+// Smallest 64-bit value over the 64 lanes, wave-uniform (all lanes active), in
+// the steps of wave_scan_dpp.
+__device__ __forceinline__ uint64_t wave_all_min64(uint64_t v) {
+  v = min64_step<0x111, 0xF>(v);
+  v = min64_step<0x112, 0xF>(v);
+  v = min64_step<0x114, 0xF>(v);
+  v = min64_step<0x118, 0xF>(v);
+  v = min64_step<0x142, 0xA>(v);
+  v = min64_step<0x143, 0xC>(v);
+  return (static_cast<uint64_t>(lane63(static_cast<uint32_t>(v >> 32))) << 32) | lane63(static_cast<uint32_t>(v));
 }
 
 // ---------------------------------------------------------------------------
@@ -330,8 +374,8 @@ __device__ __noinline__ Selected wave_select_compact(uint64_t* pool, int n, int 
     vor |= x;
     vand &= x;
   }
-  vor = wave_or64(vor);
-  vand = wave_and64(vand);
+  vor = wave_all_or64(vor);
+  vand = wave_all_and64(vand);
   if (vor == vand) return Selected{vand, -1};   // all keys equal: they were not unique
   int hb = 63 - __clzll(static_cast<long long>(vor ^ vand));
   uint64_t pmask = ~((2ull << hb) - 1ull);       // bits above hb are common
@@ -350,17 +394,17 @@ __device__ __noinline__ Selected wave_select_compact(uint64_t* pool, int n, int 
     const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
     const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
     const uint32_t lsum = c0 + c1 + c2 + c3;
-    const uint32_t incl = wave_suffix_sum(lsum, lane);
-    const uint32_t s3 = incl - lsum + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
+    const uint32_t pre = wave_prefix_sum_dpp(lsum);
+    const uint32_t s3 = lane63(pre) - pre + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
     const int local = s3 >= krem ? 4 * lane + 3
                     : s2 >= krem ? 4 * lane + 2
                     : s1 >= krem ? 4 * lane + 1
                     : s0 >= krem ? 4 * lane : -1;
-    const int dstar = wave_max_i32(local);
+    const int dstar = wave_all_max_i32(local);
     if (dstar < 0) return Selected{prefix, -1};  // fewer matching keys than krem
     const int sel = dstar & 3;
     const uint32_t my_suffix = sel == 0 ? s0 : sel == 1 ? s1 : sel == 2 ? s2 : s3;
-    const uint32_t suffix_d = __shfl(my_suffix, dstar >> 2, 64);
+    const uint32_t suffix_d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(my_suffix), dstar >> 2));
     const uint32_t cnt_d = hist[dstar];
     krem -= suffix_d - cnt_d;
     prefix |= static_cast<uint64_t>(dstar) << shift;

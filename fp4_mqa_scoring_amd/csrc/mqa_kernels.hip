@@ -469,9 +469,7 @@ __device__ __forceinline__ void for_blocks_in_window(int t, int start, int end, 
 __device__ __forceinline__ uint64_t wave_min_key(const uint64_t* pool, int n, int lane) {
   uint64_t m = ~0ull;
   for (int i = lane; i < n; i += 64) m = min(m, pool[i]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = min(m, shfl_xor_u64(m, o));
-  return m;
+  return wave_all_min64(m);
 }
 
 

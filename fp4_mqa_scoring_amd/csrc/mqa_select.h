@@ -17,7 +17,7 @@ namespace mqa {
 template <int NT>
 struct BlockScratch {
   uint64_t red64[2][NT / 64];
-  uint32_t red32[NT / 64];
+  uint32_t digit[4];   // the select's chosen digit: bin, keys at or above it, keys in it
   int32_t redi[NT / 64];
   uint32_t wtot[NT / 64];
 };
@@ -25,8 +25,8 @@ struct BlockScratch {
 template <int NT>
 __device__ __forceinline__ void block_or_and(uint64_t& vor, uint64_t& vand, BlockScratch<NT>& s) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  vor = wave_or64(vor);
-  vand = wave_and64(vand);
+  vor = wave_all_or64(vor);
+  vand = wave_all_and64(vand);
   if (lane == 0) {
     s.red64[0][w] = vor;
     s.red64[1][w] = vand;
@@ -45,7 +45,7 @@ __device__ __forceinline__ void block_or_and(uint64_t& vor, uint64_t& vand, Bloc
 template <int NT>
 __device__ __forceinline__ int block_max_i32(int v, BlockScratch<NT>& s) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_max_i32(v);
+  v = wave_all_max_i32(v);
   if (lane == 0) s.redi[w] = v;
   __syncthreads();
   int r = INT_MIN;
@@ -59,7 +59,8 @@ __device__ __forceinline__ int block_max_i32(int v, BlockScratch<NT>& s) {
 template <int NT>
 __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, BlockScratch<NT>& s) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  v = wave_suffix_sum(v, lane);
+  const uint32_t pre = wave_prefix_sum_dpp(v);
+  v = lane63(pre) - pre + v;
   if (lane == 0) s.wtot[w] = v;
   __syncthreads();
   uint32_t add = 0;
@@ -71,21 +72,43 @@ __device__ __forceinline__ uint32_t block_suffix_sum(uint32_t v, BlockScratch<NT
 }
 
 // Core of the selection: visit(f) calls f(key) for every valid key the calling
-// thread holds.
+// thread holds. Each digit pass takes three barriers: the histogram is complete;
+// the wave totals of the bin counts are posted; the one bin where the count of
+// keys at or above it first reaches the remaining rank is posted (its thread
+// finds it alone, since that count falls by bin), and every thread clears the
+// bins it read for the next pass. The wave-level sums and reductions go through
+// DPP. hist holds 2^DBITS counters.
 template <int NT, int DBITS, class Visit>
 __device__ uint64_t block_radix_select_core(const Visit& visit, int k, uint32_t* hist, BlockScratch<NT>& s,
                                             bool* ok) {
   constexpr int BINS = 1 << DBITS;
-  constexpr int BPT = BINS / NT;  // bins per thread
+  constexpr int BPT = BINS / NT;  // bins per thread: [tid BPT, tid BPT + BPT)
+  constexpr int NW = NT / 64;
   static_assert(BPT >= 1 && BINS % NT == 0, "bins must be a multiple of threads");
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   uint64_t vor = 0, vand = ~0ull;
   visit([&](uint64_t x) {
     vor |= x;
     vand &= x;
   });
-  block_or_and<NT>(vor, vand, s);
+  vor = wave_all_or64(vor);
+  vand = wave_all_and64(vand);
+  if (lane == 0) {
+    s.red64[0][w] = vor;
+    s.red64[1][w] = vand;
+  }
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) hist[tid * BPT + j] = 0u;
+  __syncthreads();
+  vor = 0;
+  vand = ~0ull;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    vor |= s.red64[0][i];
+    vand &= s.red64[1][i];
+  }
   if (vor == vand) {   // at most one distinct valid key
+    __syncthreads();   // red64 is read before anyone returns
     *ok = (k == 1);
     return vand;
   }
@@ -95,8 +118,6 @@ __device__ uint64_t block_radix_select_core(const Visit& visit, int k, uint32_t*
   uint32_t krem = static_cast<uint32_t>(k);
   for (;;) {
     const int shift = hb >= DBITS - 1 ? hb - (DBITS - 1) : 0;
-    for (int b = tid; b < BINS; b += NT) hist[b] = 0u;
-    __syncthreads();
     visit([&](uint64_t x) {
       if ((x & pmask) == prefix) atomicAdd(&hist[static_cast<uint32_t>(x >> shift) & (BINS - 1)], 1u);
     });
@@ -108,28 +129,33 @@ __device__ uint64_t block_radix_select_core(const Visit& visit, int k, uint32_t*
       c[j] = hist[tid * BPT + j];
       tsum += c[j];
     }
-    const uint32_t incl = block_suffix_sum<NT>(tsum, s);
-    uint32_t suf = incl - tsum;   // suffix strictly after this thread's bins
-    int local = -1;
-    uint32_t local_suffix = 0;
+    const uint32_t pre = wave_prefix_sum_dpp(tsum);
+    const uint32_t wave_total = lane63(pre);
+    if (lane == 0) s.wtot[w] = wave_total;
+    if (tid == 0) s.digit[0] = ~0u;   // no bin reaches krem unless a thread posts one
+    __syncthreads();
+    uint32_t suf = wave_total - pre;   // keys in the bins of the wave's later lanes
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+      if (i > w) suf += s.wtot[i];
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j) {
+      const uint32_t above = suf;   // keys in bins after bin tid BPT + j
       suf += c[j];
-      if (suf >= krem && local < 0) {
-        local = tid * BPT + j;
-        local_suffix = suf;
+      if (suf >= krem && above < krem) {
+        s.digit[0] = static_cast<uint32_t>(tid * BPT + j);
+        s.digit[1] = suf;
+        s.digit[2] = c[j];
       }
+      hist[tid * BPT + j] = 0u;
     }
-    const int dstar = block_max_i32<NT>(local, s);
-    if (dstar < 0) {
+    __syncthreads();
+    const uint32_t dstar = s.digit[0];
+    if (dstar == ~0u) {
       *ok = false;
       return prefix;
     }
-    if (local == dstar) s.red32[0] = local_suffix;
-    __syncthreads();
-    const uint32_t suffix_d = s.red32[0];
-    const uint32_t cnt_d = hist[dstar];
-    __syncthreads();
+    const uint32_t suffix_d = s.digit[1], cnt_d = s.digit[2];
     krem -= suffix_d - cnt_d;
     prefix |= static_cast<uint64_t>(dstar) << shift;
     pmask |= static_cast<uint64_t>(BINS - 1) << shift;

@@ -220,6 +220,29 @@ def test_scan_shares_span_many_rows():
     check_decode(d, base, rows=rows + [0, 1, 2, 6, 19998], where="shares over many rows")
 
 
+def test_scan_shares_with_more_rows_than_half_the_waves():
+    """3,000 long rows (600..1,200 positions, K = 512): more long rows than half
+    the gated scan's waves, fewer rows than the plan keeps in LDS, so the plan
+    gives the waves equal shares of the concatenated page list (a share runs
+    over two or three rows). Bit-equal to the no-prefilter run on every row;
+    sampled rows against the oracle."""
+    _need_gpu()
+    K = 512
+    d = synth.make_decode_inputs(1500, 2, 600, 1200, K, seed=3131)
+    n = d.lengths()
+    assert (n > K).sum() == d.Q == 3000
+    t = _dev(d)
+    mqa.mqa_fp4_status()
+    base = run_decode(t, K)
+    got = run_decode(t, K, flags=mqa.FLAG_NO_PREFILTER)
+    assert mqa.mqa_fp4_status() == 0
+    assert np.all(base[2] == K)
+    for a, b in zip(base, got):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    rows = sorted(np.random.default_rng(11).choice(d.Q, 40, replace=False).tolist())
+    check_decode(d, base, rows=rows + [0, d.Q - 1], where="shares over 3,000 rows")
+
+
 @pytest.mark.parametrize("K", [512, 1024])
 def test_windows_beyond_the_sample_budget(K):
     """Windows of 140,000..300,000 positions (2,188..4,688 pages): the per-row
