@@ -33,11 +33,15 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // gives score descending, index ascending; NaN below numbers; +0 above -0.
 // Larger key = ranks first. Keys of distinct positions are distinct.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_bits(float s) {
+// order_bits of a score that is not NaN (a NaN's bits land in a wrong class here).
+__device__ __forceinline__ uint32_t order_bits_finite(float s) {
   const uint32_t b = __float_as_uint(s);
   // non-negative (sign 0): set the top bit; negative (and -0): flip all bits
-  const uint32_t o = b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
-  return __builtin_isnan(s) ? 0u : o;                    // every NaN: lowest class
+  return b ^ (static_cast<uint32_t>(static_cast<int32_t>(b) >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t order_bits(float s) {
+  return __builtin_isnan(s) ? 0u : order_bits_finite(s);   // every NaN: lowest class
 }
 
 __device__ __forceinline__ uint64_t make_key(float s, uint32_t pos) {

@@ -107,9 +107,9 @@ struct ScanArgs {
   const float* weights;
   const uint8_t* k_pages;
   const uint8_t* k_scale;
-  int64_t P_phys;
+  int32_t P_phys;   // page counts fit int32: the host checks 64 P_phys and 64 P_log against INT32_MAX,
   const int32_t* page_table;
-  int64_t P_log;
+  int32_t P_log;    // so the kernels' page tests are 32-bit scalar compares
   const int32_t* row_start;
   const int32_t* row_end;
   const int32_t* row_state;
@@ -234,10 +234,13 @@ struct BlockDma {
 
   // Lane l holds the page-table entry of page l % 4 of block t (-1 beyond the table).
   // (Logical page indices fit in int32: the host checks 64 * P_log <= INT32_MAX.)
+  // Addresses are a uniform base plus a 32-bit unsigned lane offset, so the loads
+  // take a scalar base and no 64-bit address arithmetic per lane.
   using Ent = int32_t;
   __device__ __forceinline__ Ent entries(const ScanArgs& a, int t, int lane) const {
     const int lp = t * kTilePages + (lane & 3);
-    return lp < a.P_log ? a.page_table[lp] : -1;
+    const uint32_t off = static_cast<uint32_t>(lp) * 4u;
+    return lp < a.P_log ? *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(a.page_table) + off) : -1;
   }
 
   __device__ __forceinline__ void issue(const ScanArgs& a, const Ent& ent, uint8_t* codes, uint8_t* scales,
@@ -245,10 +248,11 @@ struct BlockDma {
     const int32_t e = __builtin_amdgcn_readlane(ent, wave >> 1);
     if (e < 0 || e >= a.P_phys) return;
     const uint8_t* page = a.k_pages + static_cast<size_t>(e) * (kPage * kVecBytes);
-    __builtin_amdgcn_global_load_lds(page + src0, codes + run * kVecBytes, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(page + src1, codes + (run + 16) * kVecBytes, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(page + static_cast<uint32_t>(src0), codes + run * kVecBytes, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(page + static_cast<uint32_t>(src1), codes + (run + 16) * kVecBytes, 16, 0, 0);
     if (lane < 32)
-      __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e) * (kPage * kVecScales) + src_sc,
+      __builtin_amdgcn_global_load_lds(a.k_scale + static_cast<size_t>(e) * (kPage * kVecScales) +
+                                           static_cast<uint32_t>(src_sc),
                                        scales + run * kVecScales, 4, 0, 0);
   }
 };
@@ -738,12 +742,23 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
       const uint64_t win = inside ? ~0ull : window_lanes(p0, start, end);
       uint64_t msk = __ballot(!(sc < gate_f)) & win;
       if (msk == 0) return;
-      const uint64_t key = make_key(sc, static_cast<uint32_t>(p0 + lane));
-      msk &= __ballot(key > gate);
-      if (msk == 0) return;
+      // A score strictly above the gate's score (as floats) has a key above the
+      // gate whatever its position, and is not NaN: when every lane the prefilter
+      // passed is such a score, those lanes are the candidates and their keys need
+      // no NaN class. Otherwise (a lane at the gate's score, a NaN, a gate in the
+      // NaN class) the exact 64-bit key test decides.
+      uint32_t hi = order_bits_finite(sc);
+      const uint32_t lo32 = ~static_cast<uint32_t>(p0) - static_cast<uint32_t>(lane);   // ~(p0 + lane)
+      if ((__ballot(sc > gate_f) & win) != msk) {
+        if (__builtin_isnan(sc)) hi = 0u;   // NaN class: as order_bits
+        msk &= __ballot(((static_cast<uint64_t>(hi) << 32) | lo32) > gate);
+        if (msk == 0) return;
+      }
+      const uint64_t key = (static_cast<uint64_t>(hi) << 32) | lo32;   // make_key(sc, p0 + lane)
       const int cnt = __popcll(msk);
       if (sf + cnt > kScanStage) flush();
-      if ((msk >> lane) & 1ull) stage[sf + mbcnt64(msk)] = key;
+      // the wave-uniform mask as the lanes' predicate (no per-lane bit test)
+      if (__builtin_amdgcn_inverse_ballot_w64(msk)) stage[sf + mbcnt64(msk)] = key;
       sf += cnt;
     });
   });
@@ -1374,9 +1389,9 @@ static ScanArgs scan_args(const PathArgs& p, const int32_t* row_state, int32_t s
   a.weights = p.weights;
   a.k_pages = p.k_pages;
   a.k_scale = p.k_scale;
-  a.P_phys = p.P_phys;
+  a.P_phys = static_cast<int32_t>(p.P_phys);
   a.page_table = p.page_table;
-  a.P_log = p.P_log;
+  a.P_log = static_cast<int32_t>(p.P_log);
   a.row_start = p.row_start;
   a.row_end = p.row_end;
   a.row_state = row_state;
