@@ -19,8 +19,8 @@ from test_gpu_parity import check_rows
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
-N_LONG_CASES = 12
+N_CASES = 96
+N_LONG_CASES = 40
 
 
 def draw_case(seed):
