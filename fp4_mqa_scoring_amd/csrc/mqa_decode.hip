@@ -7,8 +7,9 @@
 // number handed on, an exact merge of the splits, then the page-table
 // mapping). Decode workloads are the adjacent shape the pages leave on the
 // older path ("[AMD][DSv4] Add experimental AITER FP4 streaming TopK", Changes
-// / Scope) and whose graph-capture support they defer ([P2] Scope); this entry
-// point takes its scratch from the caller, never allocates or synchronises,
+// / Scope) and whose graph-capture support they defer ("[FlyDSL][DSv4]
+// Prototype FP4 MQA streaming TopK", Scope); this entry point takes its
+// scratch from the caller, never allocates or synchronises,
 // and reports row failures only on the device, so it can be captured into a
 // HIP graph and replayed.
 //
@@ -123,23 +124,16 @@ __device__ __forceinline__ void copy_page(const DecArgs& a, int32_t e, uint8_t* 
                                    0, kNonTemporal);
 }
 
-// fp32 scores of the 64 positions of one LDS page image: lane l, position l.
-__device__ __forceinline__ float score_page(const QRow& qr, const uint8_t* codes, const uint8_t* scales,
-                                            const LaneOffsets& lo) {
-  const GroupAcc g0 = mfma_group<0>(qr, codes, scales, lo);
-  const float h0 = head_partial(qr, g0.d0, g0.d1);
-  const GroupAcc g1 = mfma_group<1>(qr, codes, scales, lo);
-  const float h1 = head_partial(qr, g1.d0, g1.d1);
-  return combine_halves(h0, h1);
-}
-
-// The gated scan's scoring of one page, its LDS reads in inline asm. The
-// compiler inserts a wait for every outstanding LDS copy before an LDS read it
-// cannot prove independent of them, and across the scan's loop it cannot, which
-// would serialise the page stream; the scan orders its reads after the copies
-// with its own waits instead (stream_pages3). Each asm block waits for its reads
-// before it ends, and its memory clobber keeps it between the copies around it.
-// Same arithmetic, in the same order, as score_page: the scores are identical.
+// fp32 scores of the 64 positions of one LDS page image (lane l, position l),
+// its LDS reads in inline asm; used by the gate, the gated scan and the
+// fallback. The compiler inserts a wait for every outstanding LDS copy before
+// an LDS read it cannot prove independent of them, and across the page loops
+// it cannot, which would serialise the page streams; the streams order the
+// reads after the copies with their own waits instead (stream_pages2,
+// stream_pages3). Each asm block waits for its reads before it ends, and its
+// memory clobber keeps it between the copies around it. The MFMA groups and
+// head sums are the prefill scan's (mfma_group, head_partial, combine_halves),
+// in the same order, so a position's score is the same bit for bit.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
