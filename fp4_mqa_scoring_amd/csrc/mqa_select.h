@@ -224,32 +224,45 @@ __device__ __forceinline__ void gather_at_least(const uint64_t (&x)[E], uint32_t
 // distinct non-negative positions: K position buckets between the smallest and
 // largest position (a monotone bucket function, so bucket order is position
 // order), a prefix sum of the bucket counts, a scatter into the buckets, and
-// inside each bucket a rank by counting the smaller positions: about ten
-// barriers where a bitonic network takes fifty-five (K = 1024).
+// inside each bucket a rank by counting the smaller positions. Six barriers
+// (the extremes and the cleared buckets share one, the prefix sum takes one
+// through DPP wave sums) where a bitonic network takes fifty-five (K = 1024).
 template <int K, int NT>
 __device__ __forceinline__ void block_position_sort(uint64_t* v) {
+  constexpr int NW = NT / 64;
   __shared__ uint64_t s_tmp[K];
   __shared__ uint32_t s_start[K];
   __shared__ uint32_t s_fill[K];
-  __shared__ BlockScratch<NT> s;
-  const int tid = threadIdx.x;
+  __shared__ int32_t s_hi[NW], s_nlo[NW];
+  __shared__ uint32_t s_wsum[NW];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   int hi = INT_MIN, nlo = INT_MIN;
   for (int i = tid; i < K; i += NT) {
     const int p = static_cast<int>(v[i] >> 32);
     hi = max(hi, p);
     nlo = max(nlo, -p);
   }
-  hi = block_max_i32<NT>(hi, s);
-  const int lo = -block_max_i32<NT>(nlo, s);
-  const float scale = static_cast<float>(K) / (static_cast<float>(hi - lo) + 1.0f);
-  auto bucket = [&](uint64_t x) -> int {
-    return min(K - 1, static_cast<int>(static_cast<float>(static_cast<int>(x >> 32) - lo) * scale));
-  };
+  hi = wave_all_max_i32(hi);
+  nlo = wave_all_max_i32(nlo);
+  if (lane == 0) {
+    s_hi[w] = hi;
+    s_nlo[w] = nlo;
+  }
   for (int b = tid; b < K; b += NT) {
     s_start[b] = 0u;
     s_fill[b] = 0u;
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    hi = max(hi, s_hi[i]);
+    nlo = max(nlo, s_nlo[i]);
+  }
+  const int lo = -nlo;
+  const float scale = static_cast<float>(K) / (static_cast<float>(hi - lo) + 1.0f);
+  auto bucket = [&](uint64_t x) -> int {
+    return min(K - 1, static_cast<int>(static_cast<float>(static_cast<int>(x >> 32) - lo) * scale));
+  };
   for (int i = tid; i < K; i += NT) atomicAdd(&s_start[bucket(v[i])], 1u);
   __syncthreads();
   constexpr int B = (K + NT - 1) / NT;   // buckets per thread: [tid B, tid B + B)
@@ -261,7 +274,13 @@ __device__ __forceinline__ void block_position_sort(uint64_t* v) {
     c[j] = b < K ? s_start[b] : 0u;
     tsum += c[j];
   }
-  uint32_t run = static_cast<uint32_t>(K) - block_suffix_sum<NT>(tsum, s);   // keys in earlier buckets
+  const uint32_t pre = wave_prefix_sum_dpp(tsum);   // inclusive, over the wave's lanes
+  if (lane == 63) s_wsum[w] = pre;
+  __syncthreads();
+  uint32_t run = pre - tsum;   // keys in earlier buckets
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < w) run += s_wsum[i];
 #pragma unroll
   for (int j = 0; j < B; ++j) {
     const int b = tid * B + j;
