@@ -549,6 +549,55 @@ def test_logits_selector_total_order_on_special_value_arrays(S, lo, hi):
                 assert np.array_equal(got[~isnan], ref[~isnan]) and np.all(np.isnan(score[r][isnan]))
 
 
+@pytest.mark.parametrize("S", [4096, 40960])
+def test_logits_selector_on_adversarial_digit_patterns(S):
+    """Logit rows aimed at the exact radix select's digit logic, must equal the
+    oracle's selection exactly: distinct values one ulp apart above 1.0 and
+    below -1.0 (keys that differ only in their lowest score bits), two-valued
+    rows where the larger value holds exactly K-1, K and K+1 positions (the K-th
+    key sits at a tie, just below it, just above it), +0 and every subnormal
+    bit pattern from 1 to 4095 (each ten times over 40,960 positions), +0 / -0
+    with 300 ones, and a few clusters one ulp apart. Windows of 4,096 positions
+    take the multi-pass select, windows of 40,960 the sampled gate and the LDS
+    candidate pass."""
+    _need_gpu()
+    import torch
+    rng = np.random.default_rng(101 + S)
+    perm = lambda: rng.permutation(S).astype(np.uint32)
+    base = [
+        (np.float32(1.0).view(np.uint32) + perm()).view(np.float32),
+        (np.float32(-1.0).view(np.uint32) + perm()).view(np.float32),
+        (perm() % 4096).view(np.float32),
+        rng.choice(np.array([3.0, 2.0, np.nextafter(np.float32(2.0), np.float32(3.0)), 1.0], np.float32), S),
+    ]
+    z = np.where(rng.random(S) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    z[rng.choice(S, 300, replace=False)] = 1.0
+    base.append(z)
+    pt = rng.permutation(S // 64).astype(np.int32)
+    for K in (512, 1024):
+        rows = list(base)
+        for c in (K - 1, K, K + 1):                     # the larger value held by exactly c positions
+            r = np.full(S, np.float32(0.5), np.float32)
+            r[rng.choice(S, c, replace=False)] = 0.75
+            rows.append(r)
+        lg = np.ascontiguousarray(np.stack(rows))
+        Q = lg.shape[0]
+        st = np.zeros(Q, np.int32)
+        st[1::2] = 37                                    # some windows start off a page boundary
+        en = np.full(Q, S, np.int32)
+        outs = mqa.alloc_outputs(Q, K, "cuda", with_score=True)
+        mqa.mqa_fp4_logits_topk(torch.from_numpy(lg).cuda(), torch.from_numpy(pt).cuda(), S // 64,
+                                torch.from_numpy(st).cuda(), torch.from_numpy(en).cuda(), K, *outs)
+        raw, slot, cnt, score = [t.cpu().numpy() for t in outs]
+        assert mqa.mqa_fp4_status() == 0
+        for r in range(Q):
+            c, want = oracle.select_topk(lg[r, st[r]:en[r]].astype(np.float64), int(st[r]), K)
+            assert cnt[r] == c == K, (S, K, r)
+            assert np.array_equal(raw[r], want), (S, K, r)
+            assert np.array_equal(slot[r], expected_slots(want, pt)), (S, K, r)
+            assert np.array_equal(score[r].view(np.uint32), lg[r, want].view(np.uint32)), (S, K, r)
+
+
 def test_position_sort_on_clustered_selections():
     """The emit orders a row's selection by position with position buckets
     between its smallest and largest position; selections packed into a few
