@@ -57,6 +57,31 @@ def test_multi_sequence_rows_match_the_oracle(K, rps):
     assert mqa.mqa_fp4_status() == 0
 
 
+def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
+    """Rows whose scores hold +-inf and NaN (a weight of +-inf gives +-inf where
+    the head's dot is positive and NaN where it is 0; a NaN weight makes every
+    score NaN, so the selection is the first K positions): the gate, the scan's
+    exact key test on NaN classes and the merge order them as the oracle does,
+    and the gated, ungated and forced-underfill runs agree bit for bit."""
+    _need_gpu()
+    K = 1024
+    d = synth.make_decode_inputs(6, 1, 3000, 9000, K, seed=515)
+    d.weights[0, 3] = np.inf
+    d.weights[1, 10] = -np.inf
+    d.weights[2, 40] = np.nan
+    d.weights[3, 0], d.weights[3, 1] = np.inf, -np.inf
+    t = _dev(d)
+    base = run_decode(t, K)
+    raw, slot, cnt, _ = base
+    for r in range(d.Q):
+        check_rows(d.view(int(d.seq_of_row[r])), [r], raw, slot, cnt, None, where=f"special weights row {r}")
+    for flags in (mqa.FLAG_NO_PREFILTER, mqa.FLAG_FORCE_UNDERFILL):
+        got = run_decode(t, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+    assert mqa.mqa_fp4_status() == 0
+
+
 def test_splits_do_not_change_outputs():
     _need_gpu()
     d = synth.make_decode_inputs(5, 2, 2000, 12000, 1024, seed=7)
