@@ -82,6 +82,34 @@ def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
     assert mqa.mqa_fp4_status() == 0
 
 
+@pytest.mark.parametrize("K", [512, 1024])
+def test_sliding_windows_match_the_oracle(K):
+    """Windows that start inside the sequence (sliding windows), most of them
+    off a page boundary: 14 sequences x 2 rows, window lengths from just above
+    K to 40,000 positions and a few short ones, starts anywhere before the
+    end. Every row against the oracle through its sequence's table, and the
+    gated, ungated and forced-underfill runs bit for bit equal."""
+    _need_gpu()
+    d = synth.make_decode_inputs(14, 2, 6000, 60000, K, seed=2600 + K)
+    rng = np.random.default_rng(2700 + K)
+    for r in range(d.Q):
+        end = int(d.row_end[r])
+        if r % 7 == 3:
+            n = int(rng.integers(1, K + 1))                # short: at most K positions
+        else:
+            n = int(rng.integers(K + 1, min(40000, end) + 1))
+        d.row_start[r] = end - n
+    assert np.any(d.row_start % 64 != 0) and np.any(d.row_start > 0)
+    t = _dev(d)
+    base = run_decode(t, K)
+    check_decode(d, base, where=f"sliding K={K}")
+    for flags in (mqa.FLAG_NO_PREFILTER, mqa.FLAG_FORCE_UNDERFILL):
+        got = run_decode(t, K, flags=flags)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), hex(flags)
+    assert mqa.mqa_fp4_status() == 0
+
+
 def test_splits_do_not_change_outputs():
     _need_gpu()
     d = synth.make_decode_inputs(5, 2, 2000, 12000, 1024, seed=7)
