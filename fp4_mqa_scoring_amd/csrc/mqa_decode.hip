@@ -639,7 +639,7 @@ __global__ void __launch_bounds__(kDecThreads, 3) decode_gscan_kernel(DecArgs a)
     const uint32_t seg_off = woff;
     const bool to_fallback = a.w.cand_n[row] > static_cast<uint32_t>(a.cap);   // nothing to scan
     uint64_t held[kLaneSlots];
-    int nh = 0;   // keys this lane holds
+    int nh = 0;   // keys this lane holds, in held[0 .. nh-1] (newest first)
     auto flush = [&]() {
       uint64_t m[kLaneSlots];
       uint32_t total = 0;
@@ -679,15 +679,23 @@ __global__ void __launch_bounds__(kDecThreads, 3) decode_gscan_kernel(DecArgs a)
       const uint64_t win = (p0 >= start && p0 + kPage <= end) ? ~0ull : window_lanes(p0, start, end);
       uint64_t msk = __ballot(!(sc < gate_f)) & win;   // superset of key > gate
       if (msk == 0) return;
-      const uint64_t key = make_key(sc, static_cast<uint32_t>(p0 + lane));
-      msk &= __ballot(key > gate);
-      if (msk == 0) return;
-      const bool mine = (msk >> lane) & 1ull;
-      if (__ballot(mine && nh == kLaneSlots) != 0ull) flush();
-      if (mine) {
+      // as in the prefill scan: lanes strictly above the gate's score are above
+      // the gate and not NaN; otherwise the exact 64-bit key test decides
+      uint32_t hi = order_bits_finite(sc);
+      const uint32_t lo32 = ~static_cast<uint32_t>(p0) - static_cast<uint32_t>(lane);   // ~(p0 + lane)
+      if ((__ballot(sc > gate_f) & win) != msk) {
+        if (__builtin_isnan(sc)) hi = 0u;
+        msk &= __ballot(((static_cast<uint64_t>(hi) << 32) | lo32) > gate);
+        if (msk == 0) return;
+      }
+      const uint64_t key = (static_cast<uint64_t>(hi) << 32) | lo32;   // make_key(sc, p0 + lane)
+      // the wave-uniform mask as the lanes' predicate
+      if ((__ballot(nh == kLaneSlots) & msk) != 0ull) flush();
+      if (__builtin_amdgcn_inverse_ballot_w64(msk)) {
+        // shift register (static register names): held[0 .. nh-1] are the lane's keys
 #pragma unroll
-        for (int j = 0; j < kLaneSlots; ++j)
-          if (nh == j) held[j] = key;   // static register names
+        for (int j = kLaneSlots - 1; j > 0; --j) held[j] = held[j - 1];
+        held[0] = key;
         ++nh;
       }
     });
