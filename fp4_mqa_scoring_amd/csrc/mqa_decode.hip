@@ -70,7 +70,7 @@ struct DecArgs {
   const float* weights;
   const uint8_t* k_pages;
   const uint8_t* k_scale;
-  int64_t P_phys;
+  int32_t P_phys;   // fits int32 (the host checks 64 P_phys against INT32_MAX): a scalar page check
   const int32_t* block_table;
   int64_t max_pages;
   const int32_t* seq_of_row;
@@ -1017,7 +1017,7 @@ hipError_t launch_decode(const PathArgs& p, const DecodeScratch& w, int32_t spli
   a.weights = p.weights;
   a.k_pages = p.k_pages;
   a.k_scale = p.k_scale;
-  a.P_phys = p.P_phys;
+  a.P_phys = static_cast<int32_t>(p.P_phys);
   a.block_table = p.page_table;
   a.max_pages = p.P_log;
   a.seq_of_row = p.seq_of_row;
