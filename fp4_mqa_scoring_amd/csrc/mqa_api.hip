@@ -308,6 +308,7 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st, bool use_st
   g.count = reinterpret_cast<uint32_t*>(base + lay.count_off);
   g.fb_list = reinterpret_cast<int32_t*>(base + lay.list_off);
   g.fb_count = reinterpret_cast<int32_t*>(base + lay.listn_off);
+  g.work = reinterpret_cast<int32_t*>(base + lay.listn_off + 128);   // same 256-byte slot, its own line
   g.fb_cnt = reinterpret_cast<int32_t*>(base + lay.fbcnt_off);
   g.cand = reinterpret_cast<uint64_t*>(base + lay.cand_off);
   record_stage(0, st);
@@ -315,7 +316,7 @@ int32_t run_fused(const PathArgs& p, uint32_t flags, hipStream_t st, bool use_st
   record_stage(1, st);
   for (int stage = 0; stage < 5 && rc == MQA_OK; ++stage) {
     rc = hip_rc(mqa::launch_gated_stage(p, g, splits, calib_splits, calib_mode, (flags & MQA_FLAG_NO_FALLBACK) != 0,
-                                        stage, st));
+                                        stage, info.cus, st));
     if (stage <= 1) record_stage(2 + stage, st);   // after calibration, after the scan
   }
   record_stage(4, st);

@@ -26,6 +26,8 @@
 // Implementation (a calibrated filter of candidates, exact and stable selection,
 // the page map, failing closed); "[FlyDSL][DSv4] Prototype FP4 MQA streaming TopK"
 // (ROCm/aiter PR 5282), Changes and Scope.
+#include <atomic>
+
 #include "mqa_device.h"
 #include "mqa_launch.h"
 #include "mqa_select.h"
@@ -125,6 +127,7 @@ struct CandArgs {
   int32_t* fb_list;      // [Q] rows sent to the exact fallback
   int32_t* fb_count;     // [1]
   int32_t* fb_cnt;       // [Q, 4] per (row, fallback split) key counts
+  int32_t* work;         // [1] next (split, tile) item of the gated scan; zeroed by the calibration
   int32_t cap;
   int32_t no_fallback;   // fail closed instead of listing rows for the fallback
 };
@@ -493,6 +496,7 @@ __device__ __forceinline__ uint64_t wave_min_key(const uint64_t* pool, int n, in
 // ---------------------------------------------------------------------------
 template <int K>
 __global__ void __launch_bounds__(kCtaThreads, 4) calib_kernel(ScanArgs a, CandArgs c, int mode) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *c.work = 0;   // the scan's item counter
   MQA_BLOCK_BUFFERS;
   __shared__ uint64_t s_pool[kRowsPerCta][kCalCap];
   __shared__ uint32_t s_hist[kRowsPerCta][256];
@@ -669,16 +673,34 @@ __global__ void __launch_bounds__(64 * kCombineRows) calib_combine_kernel(ScanAr
   }
 }
 
+// Split `split` of [u0, u1) when earlier splits take larger shares: split s of
+// S gets (S - s) / (S (S + 1) / 2) of the blocks, so the items the gated scan
+// hands out last are the shortest.
+__device__ __forceinline__ BlockSeq split_range_tapered(int u0, int u1, int split, int splits) {
+  const int64_t nt = u1 - u0, S = splits;
+  auto at = [&](int64_t s) { return u0 + static_cast<int>(nt * (s * (2 * S - s + 1)) / (S * (S + 1))); };
+  const int a = at(split), b = at(split + 1);
+  return BlockSeq{a, b - a};
+}
+
 // ---------------------------------------------------------------------------
 // Gated scan: every score block of the split; keys above the row's gate are
 // staged per wave in LDS and appended to the row's candidate buffer (one global
 // atomic per flush). Appends beyond the buffer are dropped but still counted,
 // which the merge detects as an overflow.
+// Items are (split, tile) pairs in split-major order. With at least four items
+// per resident CTA the launch is persistent: a resident grid takes items from
+// one counter, and the splits are tapered so the shortest items go last.
+// Workgroups are bound to XCDs round-robin and the XCDs run the same work at
+// speeds up to ~5% apart, so one CTA per item left the fast XCDs idle for the
+// last ~0.4 ms at the headline shape; from a common counter the fast XCDs take
+// more items. With fewer items per CTA there is little to rebalance, and one
+// CTA per item (equal splits) measured faster.
 // ---------------------------------------------------------------------------
 template <int K>
 // Four waves per SIMD (the second launch bound is a minimum of waves per SIMD):
 // two CTAs per CU, at most 128 VGPRs.
-__global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandArgs c) {
+__global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandArgs c, int tiles, int persistent) {
   // Four block buffers (two pairs) and 128 staged keys per wave: 77,824 B, so
   // two CTAs still fit per CU.
   constexpr int kScanStage = 128;
@@ -689,80 +711,99 @@ __global__ void __launch_bounds__(kCtaThreads, 4) scan_kernel(ScanArgs a, CandAr
   __shared__ __attribute__((aligned(16))) uint8_t s_scales3[kTile * kVecScales];
   __shared__ uint64_t s_stage[kRowsPerCta][kScanStage];
   __shared__ int32_t s_lo[kRowsPerCta], s_hi[kRowsPerCta];
+  __shared__ int32_t s_item;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kRowsPerCta + wave;
-  bool active = row < a.Q && a.row_state[row] == kRowLong;
-  int start = 0, end = 0;
-  if (active) {
-    start = a.row_start[row];
-    end = a.row_end[row];
-  }
-  int u0 = 0, u1 = 0;
-  if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) return;
-  const BlockSeq seq = split_range(u0, u1, blockIdx.y, a.splits);
-  uint64_t gate = 0;
-  if (active) {
-    gate = c.gate[row];
-    if (c.count[row] > static_cast<uint32_t>(c.cap)) active = false;   // already sent to the fallback
-  }
-  QRow qr;
-  if (active)
-    load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
-              a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
-              a.weights + static_cast<size_t>(row) * kHeads, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-
-  const float gate_f = gate_floor(gate);
-  uint64_t* stage = s_stage[wave];
-  uint64_t* dst = c.cand + static_cast<size_t>(active ? row : 0) * c.cap;
-  int sf = 0;   // staged keys (wave-uniform)
-  auto flush = [&]() {
-    wave_lds_sync();
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&c.count[row], static_cast<uint32_t>(sf));
-    base = __shfl(base, 0, 64);
-    for (int i = lane; i < sf; i += 64) {
-      const uint32_t at = base + static_cast<uint32_t>(i);
-      if (at < static_cast<uint32_t>(c.cap)) dst[at] = stage[i];
+  const int items = tiles * a.splits;
+  int next = static_cast<int>(blockIdx.x);   // one item per CTA, unless persistent
+  if (persistent && threadIdx.x == 0) next = atomicAdd(c.work, 1);
+  for (;;) {
+    if (threadIdx.x == 0) s_item = next;
+    __syncthreads();
+    const int item = s_item;
+    __syncthreads();
+    if (item >= items) break;
+    const int split = item / tiles, tile = item - split * tiles;
+    const int row = tile * kRowsPerCta + wave;
+    bool active = row < a.Q && a.row_state[row] == kRowLong;
+    int start = 0, end = 0;
+    if (active) {
+      start = a.row_start[row];
+      end = a.row_end[row];
     }
-    wave_lds_sync();
-    sf = 0;
-  };
-  const LaneOffsets lo = lane_offsets(lane);
-  stream_block_pairs(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, s_codes2, s_scales2, s_codes3, s_scales3,
-                     [&](int t, const uint8_t* codes, const uint8_t* scales) {
-    if (!active) return;
-    const int tb = t * kTile;
-    if (tb >= end || tb + kTile <= start) return;
-    const bool inside = tb >= start && tb + kTile <= end;   // no window mask needed
-    score_block(qr, codes, scales, lo, [&](int blk, float sc) {
-      const int p0 = tb + 64 * blk;
-      // wave-uniform window mask; one float compare rejects almost every lane
-      const uint64_t win = inside ? ~0ull : window_lanes(p0, start, end);
-      uint64_t msk = __ballot(!(sc < gate_f)) & win;
-      if (msk == 0) return;
-      // A score strictly above the gate's score (as floats) has a key above the
-      // gate whatever its position, and is not NaN: when every lane the prefilter
-      // passed is such a score, those lanes are the candidates and their keys need
-      // no NaN class. Otherwise (a lane at the gate's score, a NaN, a gate in the
-      // NaN class) the exact 64-bit key test decides.
-      uint32_t hi = order_bits_finite(sc);
-      const uint32_t lo32 = ~static_cast<uint32_t>(p0) - static_cast<uint32_t>(lane);   // ~(p0 + lane)
-      if ((__ballot(sc > gate_f) & win) != msk) {
-        if (__builtin_isnan(sc)) hi = 0u;   // NaN class: as order_bits
-        msk &= __ballot(((static_cast<uint64_t>(hi) << 32) | lo32) > gate);
-        if (msk == 0) return;
+    int u0 = 0, u1 = 0;
+    if (!row_tile_range(s_lo, s_hi, active, start, end, wave, lane, &u0, &u1)) {
+      if (threadIdx.x == 0) next = persistent ? atomicAdd(c.work, 1) : items;
+      continue;
+    }
+    const BlockSeq seq =
+        persistent ? split_range_tapered(u0, u1, split, a.splits) : split_range(u0, u1, split, a.splits);
+    uint64_t gate = 0;
+    if (active) {
+      gate = c.gate[row];
+      if (c.count[row] > static_cast<uint32_t>(c.cap)) active = false;   // already sent to the fallback
+    }
+    QRow qr;
+    if (active)
+      load_qrow(qr, a.q + static_cast<size_t>(row) * kHeads * kVecBytes,
+                a.q_scale + static_cast<size_t>(row) * kHeads * kVecScales,
+                a.weights + static_cast<size_t>(row) * kHeads, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const float gate_f = gate_floor(gate);
+    uint64_t* stage = s_stage[wave];
+    uint64_t* dst = c.cand + static_cast<size_t>(active ? row : 0) * c.cap;
+    int sf = 0;   // staged keys (wave-uniform)
+    auto flush = [&]() {
+      wave_lds_sync();
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&c.count[row], static_cast<uint32_t>(sf));
+      base = __shfl(base, 0, 64);
+      for (int i = lane; i < sf; i += 64) {
+        const uint32_t at = base + static_cast<uint32_t>(i);
+        if (at < static_cast<uint32_t>(c.cap)) dst[at] = stage[i];
       }
-      const uint64_t key = (static_cast<uint64_t>(hi) << 32) | lo32;   // make_key(sc, p0 + lane)
-      const int cnt = __popcll(msk);
-      if (sf + cnt > kScanStage) flush();
-      // the wave-uniform mask as the lanes' predicate (no per-lane bit test)
-      if (__builtin_amdgcn_inverse_ballot_w64(msk)) stage[sf + mbcnt64(msk)] = key;
-      sf += cnt;
+      wave_lds_sync();
+      sf = 0;
+    };
+    const LaneOffsets lo = lane_offsets(lane);
+    stream_block_pairs(a, seq, s_codes0, s_scales0, s_codes1, s_scales1, s_codes2, s_scales2, s_codes3, s_scales3,
+                       [&](int t, const uint8_t* codes, const uint8_t* scales) {
+      if (!active) return;
+      const int tb = t * kTile;
+      if (tb >= end || tb + kTile <= start) return;
+      const bool inside = tb >= start && tb + kTile <= end;   // no window mask needed
+      score_block(qr, codes, scales, lo, [&](int blk, float sc) {
+        const int p0 = tb + 64 * blk;
+        // wave-uniform window mask; one float compare rejects almost every lane
+        const uint64_t win = inside ? ~0ull : window_lanes(p0, start, end);
+        uint64_t msk = __ballot(!(sc < gate_f)) & win;
+        if (msk == 0) return;
+        // A score strictly above the gate's score (as floats) has a key above the
+        // gate whatever its position, and is not NaN: when every lane the prefilter
+        // passed is such a score, those lanes are the candidates and their keys need
+        // no NaN class. Otherwise (a lane at the gate's score, a NaN, a gate in the
+        // NaN class) the exact 64-bit key test decides.
+        uint32_t hi = order_bits_finite(sc);
+        const uint32_t lo32 = ~static_cast<uint32_t>(p0) - static_cast<uint32_t>(lane);   // ~(p0 + lane)
+        if ((__ballot(sc > gate_f) & win) != msk) {
+          if (__builtin_isnan(sc)) hi = 0u;   // NaN class: as order_bits
+          msk &= __ballot(((static_cast<uint64_t>(hi) << 32) | lo32) > gate);
+          if (msk == 0) return;
+        }
+        const uint64_t key = (static_cast<uint64_t>(hi) << 32) | lo32;   // make_key(sc, p0 + lane)
+        const int cnt = __popcll(msk);
+        if (sf + cnt > kScanStage) flush();
+        // the wave-uniform mask as the lanes' predicate (no per-lane bit test)
+        if (__builtin_amdgcn_inverse_ballot_w64(msk)) stage[sf + mbcnt64(msk)] = key;
+        sf += cnt;
+      });
     });
-  });
-  if (active && sf > 0) flush();
+    // the following item is taken as this one ends, so items go to the CTAs that
+    // finish first (its latency overlaps the last flush)
+    if (threadIdx.x == 0) next = persistent ? atomicAdd(c.work, 1) : items;
+    if (active && sf > 0) flush();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1408,6 +1449,7 @@ static CandArgs cand_args(const GatedScratch& g, int K, bool no_fallback) {
   c.fb_list = g.fb_list;
   c.fb_count = g.fb_count;
   c.fb_cnt = g.fb_cnt;
+  c.work = g.work;
   c.cap = candidate_cap(K);
   c.no_fallback = no_fallback ? 1 : 0;
   return c;
@@ -1423,7 +1465,7 @@ hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int3
 
 template <int K>
 static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
-                                 int calib_mode, bool no_fallback, int stage, hipStream_t st) {
+                                 int calib_mode, bool no_fallback, int stage, int cus, hipStream_t st) {
   using G = Geometry<K>;
   const ScanArgs a = scan_args(p, g.row_state, splits);
   const CandArgs c = cand_args(g, K, no_fallback);
@@ -1443,9 +1485,22 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
                                dim3(64 * kCombineRows), 0, st>>>(a, c, static_cast<int>(cs));
       break;
     }
-    case 1:
-      scan_kernel<K><<<dim3(tiles, static_cast<unsigned>(splits)), dim3(kCtaThreads), 0, st>>>(a, c);
+    case 1: {
+      // a resident round of CTAs pulling (split, tile) items, or one CTA per item
+      static std::atomic<int> per_cu{0};
+      int occ = per_cu.load(std::memory_order_relaxed);
+      if (occ == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_kernel<K>, kCtaThreads, 0) != hipSuccess || occ < 1)
+          occ = 2;
+        per_cu.store(occ, std::memory_order_relaxed);
+      }
+      const int64_t items = static_cast<int64_t>(tiles) * splits, resident = static_cast<int64_t>(occ) * cus;
+      const int persistent = items >= 4 * resident ? 1 : 0;
+      const int64_t grid = persistent ? resident : items;
+      scan_kernel<K><<<dim3(static_cast<unsigned>(grid)), dim3(kCtaThreads), 0, st>>>(a, c, static_cast<int>(tiles),
+                                                                                      persistent);
       break;
+    }
     case 2:
       merge_kernel<K><<<dim3(static_cast<unsigned>(p.Q)), dim3(256), 0, st>>>(
           g.row_state, c, p.page_table, p.P_log, p.out_raw, p.out_slot, p.out_count, p.out_score);
@@ -1462,10 +1517,10 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
 }
 
 hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
-                              int calib_mode, bool no_fallback, int stage, hipStream_t st) {
+                              int calib_mode, bool no_fallback, int stage, int cus, hipStream_t st) {
   if (p.Q == 0) return hipSuccess;
-  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, st)
-                    : launch_gated_k<1024>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, st);
+  return p.K == 512 ? launch_gated_k<512>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, cus, st)
+                    : launch_gated_k<1024>(p, g, splits, calib_splits, calib_mode, no_fallback, stage, cus, st);
 }
 
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,

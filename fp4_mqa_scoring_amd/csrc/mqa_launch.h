@@ -39,6 +39,7 @@ struct GatedScratch {
   int32_t* fb_count;    // [1]
   int32_t* fb_cnt;      // [Q, 4]
   uint64_t* cand;       // [Q, candidate_cap(K)]
+  int32_t* work;        // [1] the gated scan's item counter
 };
 
 // Candidate keys kept per row by the fused path's gated scan. The gate is the
@@ -66,7 +67,7 @@ hipError_t launch_row_prep(const PathArgs& p, int mode, int32_t* row_state, int3
 // no_fallback the merge fails closed the rows it would list for the fallback
 // (underfill -3, overflow -4) and the list stays empty.
 hipError_t launch_gated_stage(const PathArgs& p, const GatedScratch& g, int32_t splits, int32_t calib_splits,
-                              int calib_mode, bool no_fallback, int stage, hipStream_t st);
+                              int calib_mode, bool no_fallback, int stage, int cus, hipStream_t st);
 hipError_t launch_dense_score(const PathArgs& p, const int32_t* row_state, int32_t splits, float* logits,
                               hipStream_t st);
 // Decode / multi-sequence path: per-wave streaming exact TopK over each row's
