@@ -15,6 +15,10 @@ namespace {
 // One block per CU: the issue probe asks for more LDS than half a CU holds.
 constexpr int kIssueLdsBytes = 96 * 1024;
 constexpr int kLdsProbeThreads = 512;
+// The valu-waves probe: a CU's LDS, and the most waves per SIMD it asks for
+// (the FMA loop's register count lets six waves share a SIMD).
+constexpr int kCuLdsBytes = 160 * 1024;
+constexpr int kValuProbeMaxWaves = 6;
 
 // Four independent accumulator chains per wave, one 32x32x64 FP4 MFMA each per
 // iteration. Codes and scales are arbitrary finite values.
@@ -69,6 +73,26 @@ __global__ void __launch_bounds__(1024) issue_probe_kernel(int n_mfma, int iters
     o[0] = t0;
     o[1] = t1;
     // HW_ID (wave slot, SIMD, CU, shader engine) and XCC_ID hardware registers
+    o[2] = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4))) |
+           (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 20))) << 32);
+  }
+}
+
+// Blocks of four waves (one per SIMD) that only run the FMA loop; the caller's
+// LDS request caps how many blocks share a CU, and so the waves per SIMD.
+__global__ void __launch_bounds__(256) valu_waves_probe_kernel(int iters, uint64_t* __restrict__ rec,
+                                                               float* __restrict__ sink) {
+  extern __shared__ char s_reserve[];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (threadIdx.x == 0) s_reserve[0] = 0;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const float v = fma_loop(iters, l);
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  sink[static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x] = v;
+  if (l == 0) {
+    uint64_t* o = rec + (static_cast<size_t>(blockIdx.x) * 4 + w) * 3;
+    o[0] = t0;
+    o[1] = t1;
     o[2] = static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 4))) |
            (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_s_getreg((31 << 11) | 20))) << 32);
   }
@@ -189,6 +213,27 @@ int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iter
   const unsigned threads = 256u * static_cast<unsigned>(n_mfma_waves + n_valu_waves);
   mqa::issue_probe_kernel<<<dim3(static_cast<unsigned>(g.cus)), dim3(threads), mqa::kIssueLdsBytes, st>>>(
       n_mfma_waves, iters, rec, sink);
+  return mqa::launched();
+}
+
+int32_t mqa_probe_valu_waves(int32_t waves_per_simd, int32_t iters, uint64_t* rec, float* sink, void* stream) {
+  if (waves_per_simd < 1 || waves_per_simd > mqa::kValuProbeMaxWaves || iters < 1) return MQA_ERR_BAD_SIZE;
+  if (rec == nullptr || sink == nullptr) return MQA_ERR_NULL_POINTER;
+  if (reinterpret_cast<uintptr_t>(rec) % 8 || reinterpret_cast<uintptr_t>(sink) % 4) return MQA_ERR_MISALIGNED;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  mqa::Guard g;
+  int32_t rc = g.enter(st);
+  if (rc != MQA_OK) return rc;
+  if ((rc = mqa::check_out(rec, 8, g.dev)) != MQA_OK || (rc = mqa::check_out(sink, 4, g.dev)) != MQA_OK) return rc;
+  // k blocks of this size fit a CU's 160 KB of LDS, k + 1 do not
+  const int lds = mqa::kCuLdsBytes / waves_per_simd - 1024;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(mqa::valu_waves_probe_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return MQA_ERR_HIP;
+  }
+  mqa::valu_waves_probe_kernel<<<dim3(static_cast<unsigned>(g.cus * waves_per_simd)), dim3(256), lds, st>>>(
+      iters, rec, sink);
   return mqa::launched();
 }
 

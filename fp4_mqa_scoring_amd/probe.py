@@ -32,8 +32,9 @@ def lib() -> ctypes.CDLL:
         P, i32 = ctypes.c_void_p, ctypes.c_int32
         L.mqa_probe_blocks.argtypes = [P]
         L.mqa_probe_issue.argtypes = [i32, i32, i32, P, P, P]
+        L.mqa_probe_valu_waves.argtypes = [i32, i32, P, P, P]
         L.mqa_probe_lds.argtypes = [i32, P, i32, i32, P]
-        for f in (L.mqa_probe_blocks, L.mqa_probe_issue, L.mqa_probe_lds):
+        for f in (L.mqa_probe_blocks, L.mqa_probe_issue, L.mqa_probe_valu_waves, L.mqa_probe_lds):
             f.restype = i32
         _lib = L
     return _lib
@@ -92,6 +93,23 @@ def issue(n_mfma: int, n_valu: int, iters: int, stream=None) -> dict:
             "ms": e0.elapsed_time(e1), "blocks": blocks}
 
 
+def valu_waves(waves_per_simd: int, iters: int = 4096, stream=None) -> float:
+    """Cycles per fp32 FMA of one SIMD holding waves_per_simd FMA waves (mean
+    per-SIMD span / the SIMD's FMAs), from one launch after a warm one."""
+    import torch
+    L = lib()
+    st = _stream(stream)
+    blocks = _ok(L.mqa_probe_blocks(st), "mqa_probe_blocks") * waves_per_simd
+    rec = torch.zeros((blocks, 4, 3), dtype=torch.int64, device="cuda")
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    args = (waves_per_simd, iters, ctypes.c_void_p(rec.data_ptr()), ctypes.c_void_p(sink.data_ptr()), st)
+    for _ in range(2):
+        _ok(L.mqa_probe_valu_waves(*args), "mqa_probe_valu_waves")
+    torch.cuda.synchronize()
+    spans = simd_spans(rec.cpu().numpy())
+    return float(spans.mean()) / (waves_per_simd * iters * FMA_PER_ITER)
+
+
 def issue_rates(iters: int = 4096, stream=None) -> dict:
     """Cycle rates of one SIMD: MFMAs (one and two MFMA waves), fp32 FMAs (two
     and four VALU waves), and one MFMA wave beside two VALU waves. overlap is
@@ -112,6 +130,9 @@ def issue_rates(iters: int = 4096, stream=None) -> dict:
         "cycles_per_mfma_2waves": m2["simd_cycles"] / (2 * n_mfma),
         "cycles_per_fma_2waves": v2["simd_cycles"] / (2 * n_fma),
         "cycles_per_fma_4waves": v4["simd_cycles"] / (4 * n_fma),
+        # 1..6 FMA waves per SIMD: how far more resident waves bring the VALU
+        # toward one wave64 FMA per 2 cycles
+        "cycles_per_fma_by_waves": {k: valu_waves(k, iters, stream) for k in range(1, 7)},
         "mfma_plus_2valu_cycles": mix["simd_cycles"],
         "mfma_alone_plus_2valu_alone_cycles": alone,
         "simd_mfma_valu_overlap": overlap,

@@ -45,6 +45,20 @@ int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iter
                         void* stream);
 
 /*
+ * VALU-waves probe: blocks of 256 threads, waves_per_simd per compute unit
+ * (1 <= waves_per_simd <= 6; each block's LDS request, 160 KB / waves_per_simd
+ * - 1 KB, keeps one block more off the CU), so every SIMD holds waves_per_simd
+ * waves that each issue iters x 64 independent fp32 FMAs (16 chains): the
+ * VALU issue rate of one SIMD as a function of its resident waves.
+ *   rec   uint64 [blocks * waves_per_simd, 4, 3]: per wave the shader-cycle
+ *         counter at its start and end and its hardware id, as in the issue
+ *         probe
+ *   sink  float [blocks * waves_per_simd * 256] (every element written)
+ * blocks = mqa_probe_blocks(stream).
+ */
+int32_t mqa_probe_valu_waves(int32_t waves_per_simd, int32_t iters, uint64_t* rec, float* sink, void* stream);
+
+/*
  * LDS read probe: blocks x 8 waves x iters x 2 ds_read_b128 over a 16 KB
  * score-block image. pattern 0: the scan's operand reads (chunk swizzle
  * applied), 1: a linear pattern no bank grouping makes conflict, 2: the image
