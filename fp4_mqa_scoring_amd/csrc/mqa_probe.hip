@@ -12,6 +12,8 @@
 namespace mqa {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // One block per CU: the issue probe asks for more LDS than half a CU holds.
 constexpr int kIssueLdsBytes = 96 * 1024;
 constexpr int kLdsProbeThreads = 512;
@@ -36,6 +38,25 @@ __device__ __noinline__ float mfma_loop(int iters, int l) {
   return c0[0] + c1[1] + c2[2] + c3[3];
 }
 
+// The same FLOPs per iteration as eight 16x16x128 MXFP4 MFMAs (eight chains
+// of four accumulator registers instead of four chains of sixteen).
+__device__ __noinline__ float mfma16_loop(int iters, int l) {
+  const v8i a = {l * 0x01010101, l * 0x03030303, l * 0x05050505, l * 0x07070707, 0, 0, 0, 0};
+  const v8i b = a ^ v8i{0x55555555, 0x33333333, 0x0F0F0F0F, 0x11111111, 0, 0, 0, 0};
+  const int sc = 0x7F7F7F7F;
+  v4f c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c[i], 4, 4, 0, sc, 0, sc);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += c[i][i & 3];
+  return s;
+}
+
 // Sixteen independent chains, 64 fp32 FMAs per lane per iteration.
 __device__ __noinline__ float fma_loop(int iters, int l) {
   float w[16], x[16], p[16];
@@ -58,14 +79,14 @@ __device__ __noinline__ float fma_loop(int iters, int l) {
   return s;
 }
 
-__global__ void __launch_bounds__(1024) issue_probe_kernel(int n_mfma, int iters, uint64_t* __restrict__ rec,
-                                                           float* __restrict__ sink) {
+__global__ void __launch_bounds__(1024) issue_probe_kernel(int n_mfma, int shape16, int iters,
+                                                           uint64_t* __restrict__ rec, float* __restrict__ sink) {
   extern __shared__ char s_reserve[];   // only reserved: one block per CU
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
   if (threadIdx.x == 0) s_reserve[0] = 0;
   const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  const float v = (w >> 2) < n_mfma ? mfma_loop(iters, l) : fma_loop(iters, l);
+  const float v = (w >> 2) < n_mfma ? (shape16 ? mfma16_loop(iters, l) : mfma_loop(iters, l)) : fma_loop(iters, l);
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   sink[static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x] = v;
   if (l == 0) {
@@ -193,8 +214,9 @@ int32_t mqa_probe_blocks(void* stream) {
   return rc == MQA_OK ? g.cus : rc;
 }
 
-int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
-                        void* stream) {
+namespace {
+int32_t issue_probe(int32_t n_mfma_waves, int32_t n_valu_waves, int shape16, int32_t iters, uint64_t* rec, float* sink,
+                    void* stream) {
   if (n_mfma_waves < 0 || n_valu_waves < 0 || n_mfma_waves + n_valu_waves < 1 || n_mfma_waves + n_valu_waves > 4 ||
       iters < 1)
     return MQA_ERR_BAD_SIZE;
@@ -212,8 +234,19 @@ int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iter
   }
   const unsigned threads = 256u * static_cast<unsigned>(n_mfma_waves + n_valu_waves);
   mqa::issue_probe_kernel<<<dim3(static_cast<unsigned>(g.cus)), dim3(threads), mqa::kIssueLdsBytes, st>>>(
-      n_mfma_waves, iters, rec, sink);
+      n_mfma_waves, shape16, iters, rec, sink);
   return mqa::launched();
+}
+}  // namespace
+
+int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
+                        void* stream) {
+  return issue_probe(n_mfma_waves, n_valu_waves, 0, iters, rec, sink, stream);
+}
+
+int32_t mqa_probe_issue16(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
+                          void* stream) {
+  return issue_probe(n_mfma_waves, n_valu_waves, 1, iters, rec, sink, stream);
 }
 
 int32_t mqa_probe_valu_waves(int32_t waves_per_simd, int32_t iters, uint64_t* rec, float* sink, void* stream) {

@@ -32,9 +32,11 @@ def lib() -> ctypes.CDLL:
         P, i32 = ctypes.c_void_p, ctypes.c_int32
         L.mqa_probe_blocks.argtypes = [P]
         L.mqa_probe_issue.argtypes = [i32, i32, i32, P, P, P]
+        L.mqa_probe_issue16.argtypes = [i32, i32, i32, P, P, P]
         L.mqa_probe_valu_waves.argtypes = [i32, i32, P, P, P]
         L.mqa_probe_lds.argtypes = [i32, P, i32, i32, P]
-        for f in (L.mqa_probe_blocks, L.mqa_probe_issue, L.mqa_probe_valu_waves, L.mqa_probe_lds):
+        for f in (L.mqa_probe_blocks, L.mqa_probe_issue, L.mqa_probe_issue16, L.mqa_probe_valu_waves,
+                  L.mqa_probe_lds):
             f.restype = i32
         _lib = L
     return _lib
@@ -70,22 +72,24 @@ def simd_spans(rec: np.ndarray) -> np.ndarray:
     return (hi - lo).astype(np.float64)
 
 
-def issue(n_mfma: int, n_valu: int, iters: int, stream=None) -> dict:
+def issue(n_mfma: int, n_valu: int, iters: int, stream=None, shape16: bool = False) -> dict:
     """One issue-probe launch: mean per-SIMD span in cycles and the launch's
-    wall time (events on the stream)."""
+    wall time (events on the stream). shape16: the MFMA waves issue 16x16x128
+    MFMAs (eight per iteration, the same FLOPs) instead of 32x32x64."""
     import torch
     L = lib()
+    fn = L.mqa_probe_issue16 if shape16 else L.mqa_probe_issue
     st = _stream(stream)
     blocks = _ok(L.mqa_probe_blocks(st), "mqa_probe_blocks")
     nw = 4 * (n_mfma + n_valu)
     rec = torch.zeros((blocks, nw, 3), dtype=torch.int64, device="cuda")
     sink = torch.empty(blocks * 64 * nw, dtype=torch.float32, device="cuda")
     args = (n_mfma, n_valu, iters, ctypes.c_void_p(rec.data_ptr()), ctypes.c_void_p(sink.data_ptr()), st)
-    _ok(L.mqa_probe_issue(*args), "mqa_probe_issue")          # warm (clocks, code load)
+    _ok(fn(*args), "mqa_probe_issue")                         # warm (clocks, code load)
     s = stream if stream is not None else torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    _ok(L.mqa_probe_issue(*args), "mqa_probe_issue")
+    _ok(fn(*args), "mqa_probe_issue")
     e1.record(s)
     torch.cuda.synchronize()
     spans = simd_spans(rec.cpu().numpy())
@@ -120,6 +124,8 @@ def issue_rates(iters: int = 4096, stream=None) -> dict:
     v2 = issue(0, 2, iters, stream)
     v4 = issue(0, 4, iters, stream)
     mix = issue(1, 2, iters, stream)
+    m16 = issue(1, 0, iters, stream, shape16=True)
+    mix16 = issue(1, 2, iters, stream, shape16=True)
     n_mfma = iters * MFMA_PER_ITER
     n_fma = iters * FMA_PER_ITER
     alone = m1["simd_cycles"] + v2["simd_cycles"]
@@ -136,6 +142,11 @@ def issue_rates(iters: int = 4096, stream=None) -> dict:
         "mfma_plus_2valu_cycles": mix["simd_cycles"],
         "mfma_alone_plus_2valu_alone_cycles": alone,
         "simd_mfma_valu_overlap": overlap,
+        # the same with 16x16x128 MFMAs (cycles per 32x32x64-equivalent, one wave)
+        "cycles_per_mfma32_equiv_16x16x128_1wave": m16["simd_cycles"] / n_mfma,
+        "mfma16_plus_2valu_cycles": mix16["simd_cycles"],
+        "simd_mfma16_valu_overlap": (m16["simd_cycles"] + v2["simd_cycles"] - mix16["simd_cycles"]) /
+                                    min(m16["simd_cycles"], v2["simd_cycles"]),
         # sustained MXFP4 rate of the two-wave MFMA launch (wall time by events)
         "mxfp4_tflops_measured": blocks * 4 * 2 * n_mfma * FLOP_PER_MFMA / (m2["ms"] * 1e-3) / 1e12,
     }

@@ -44,6 +44,13 @@ int32_t mqa_probe_blocks(void* stream);
 int32_t mqa_probe_issue(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
                         void* stream);
 
+/* The issue probe with the MFMA waves issuing iters x 8 independent
+ * v_mfma_scale_f32_16x16x128_f8f6f4 (MXFP4 x MXFP4, 2*16*16*128 FLOP each:
+ * the same FLOPs per iteration as mqa_probe_issue); arguments, records and
+ * errors as there. */
+int32_t mqa_probe_issue16(int32_t n_mfma_waves, int32_t n_valu_waves, int32_t iters, uint64_t* rec, float* sink,
+                          void* stream);
+
 /*
  * VALU-waves probe: blocks of 256 threads, waves_per_simd per compute unit
  * (1 <= waves_per_simd <= 6; each block's LDS request, 160 KB / waves_per_simd

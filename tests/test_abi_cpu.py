@@ -111,7 +111,8 @@ def test_probes_live_in_their_own_library(lib, probe_lib):
     header declares none and its library exports none; the probe header's
     symbols are all exported by the probe library."""
     probe_syms = sorted(set(re.findall(r"^\s*int32_t\s+(mqa_probe_\w+)\s*\(", open(PROBE_HEADER).read(), re.M)))
-    assert probe_syms == ["mqa_probe_blocks", "mqa_probe_issue", "mqa_probe_lds", "mqa_probe_valu_waves"]
+    assert probe_syms == ["mqa_probe_blocks", "mqa_probe_issue", "mqa_probe_issue16", "mqa_probe_lds",
+                          "mqa_probe_valu_waves"]
     for name in probe_syms:
         assert hasattr(probe_lib, name), name
         assert not hasattr(lib, name), name
@@ -128,6 +129,8 @@ def test_probes_reject_bad_arguments_on_host(probe_lib):
     assert L.mqa_probe_issue(1, 1, 0, p, p, None) == -4          # no iterations
     assert L.mqa_probe_issue(1, 1, 8, None, p, None) == -2
     assert L.mqa_probe_issue(1, 1, 8, ctypes.c_void_p(0x1004), p, None) == -3
+    assert L.mqa_probe_issue16(3, 2, 8, p, p, None) == -4        # more than four waves per SIMD
+    assert L.mqa_probe_issue16(1, 1, 8, None, p, None) == -2
     assert L.mqa_probe_valu_waves(0, 8, p, p, None) == -4         # no waves
     assert L.mqa_probe_valu_waves(7, 8, p, p, None) == -4         # more than six per SIMD
     assert L.mqa_probe_valu_waves(2, 0, p, p, None) == -4         # no iterations

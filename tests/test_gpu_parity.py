@@ -271,6 +271,7 @@ def test_measurement_probes_run():
     assert 16 < rates["cycles_per_mfma_2waves"] < 80 and 1 < rates["cycles_per_fma_4waves"] < 8
     assert sorted(rates["cycles_per_fma_by_waves"]) == list(range(1, 7))
     assert all(1 < c < 16 for c in rates["cycles_per_fma_by_waves"].values())
+    assert 16 < rates["cycles_per_mfma32_equiv_16x16x128_1wave"] < 80
     assert probe.lds_ms(0, blocks=64, iters=64) > 0
     host = torch.zeros(64 * 512, dtype=torch.float32)
     assert probe.lib().mqa_probe_lds(0, ctypes.c_void_p(host.data_ptr()), 64, 8, None) == -5
