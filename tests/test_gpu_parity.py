@@ -47,10 +47,9 @@ def check_rows(inp, rows, raw, slot, cnt, score=None, where=""):
         check_long_row(sigma, mag, st, K, raw[r], slot[r], int(cnt[r]), inp.page_table, tol=TOL,
                        oracle_sel=sel, where=tag)
         if score is not None and np.all(np.isfinite(sigma)):
-            ref = sigma[raw[r] - st]
-            bound = TOL * max(np.abs(sigma).max(), mag.max())
-            err = np.abs(score[r].astype(np.float64) - ref)
-            assert np.all(err <= bound), f"{tag}: score error {err.max()} > {bound}"
+            # each returned score within its own bound 1e-5 * max(|s|, m_s)
+            idx = raw[r] - st
+            check_scores(score[r], sigma[idx], mag[idx], tol=TOL, where=f"{tag} scores")
 
 
 # --- per-head dot products: bit-exact through the public API --------------------------
