@@ -638,6 +638,34 @@ def test_position_sort_on_clustered_selections():
             assert np.array_equal(slot[r], expected_slots(want, pt)), (K, r)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("K", [512, 1024])
+def test_many_rows_beyond_the_workloads(K):
+    """40,000 rows over a 4,096-position context: five times the rows of the
+    largest workload, through the row-indexed grids and the persistent scan with
+    one context split. Ragged windows with nonzero starts, empty, short and long
+    rows: every row's count, order, window and slots; every short row and 128
+    sampled rows against the oracle."""
+    _need_gpu()
+    Q, S = 40000, 4096
+    rng = np.random.default_rng(4242 + K)
+    st = rng.integers(0, S, Q)
+    en = np.minimum(st + rng.integers(0, S + 1, Q), S)
+    st[::997] = en[::997]                                   # empty rows
+    inp = synth.make_inputs(Q, S, K, 31337 + K, row_start=st.astype(np.int32), row_end=en.astype(np.int32))
+    raw, slot, cnt, score = gu.run_fused(gu.to_device(inp), K)
+    n = inp.lengths()
+    long_rows = n > K
+    assert 1000 < long_rows.sum() < Q - 1000
+    assert np.all(cnt[long_rows] == K) and np.all(cnt[~long_rows] == n[~long_rows])
+    assert np.all(np.diff(raw[long_rows], axis=1) > 0)
+    assert np.all(raw[long_rows] >= inp.row_start[long_rows, None])
+    assert np.all(raw[long_rows] < inp.row_end[long_rows, None])
+    assert np.array_equal(slot[long_rows], expected_slots(raw[long_rows], inp.page_table))
+    rows = np.union1d(np.flatnonzero(~long_rows), synth.sample_rows(inp, 128, seed=K))
+    check_rows(inp, rows, raw, slot, cnt, score, where=f"{Q} rows K={K}")
+
+
 # --- the benchmark workloads at full size -------------------------------------------------
 
 # One fused run per configuration, kept while that configuration's checks run
