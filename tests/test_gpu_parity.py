@@ -666,6 +666,24 @@ def test_many_rows_beyond_the_workloads(K):
     check_rows(inp, rows, raw, slot, cnt, score, where=f"{Q} rows K={K}")
 
 
+@pytest.mark.timeout(300)
+def test_two_million_position_context():
+    """Four rows over 2,097,152 C4 positions (32,768 pages, eight times the
+    longest workload's context): whole, trimmed, mid-size and short windows,
+    against the oracle; the ungated and the context-tiled paths bit-equal."""
+    _need_gpu()
+    Q, S, K = 4, 1 << 21, 1024
+    st = np.array([0, 123, 700_001, 1_048_000], dtype=np.int32)
+    en = np.array([S, S - 77, 1_234_567, 1_048_900], dtype=np.int32)
+    inp = synth.make_inputs(Q, S, K, 2021, row_start=st, row_end=en)
+    dev = gu.to_device(inp)
+    base = gu.run_fused(dev, K)
+    check_rows(inp, range(Q), *base, where="2M context")
+    for got in (gu.run_fused(dev, K, flags=mqa.FLAG_NO_PREFILTER), gu.run_tiled(dev, K)):
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
 # --- the benchmark workloads at full size -------------------------------------------------
 
 # One fused run per configuration, kept while that configuration's checks run
