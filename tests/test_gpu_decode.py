@@ -57,6 +57,22 @@ def test_multi_sequence_rows_match_the_oracle(K, rps):
     assert mqa.mqa_fp4_status() == 0
 
 
+@pytest.mark.timeout(300)
+def test_sequences_of_two_million_positions():
+    """Two sequences of 1.5M-2.1M C4 positions, one row each: the gate samples
+    a coarser multiple of its page stride there; rows against the oracle through
+    their tables, the ungated run bit-equal."""
+    _need_gpu()
+    K = 1024
+    d = synth.make_decode_inputs(2, 1, 1_500_000, 1 << 21, K, seed=2048)
+    t = _dev(d)
+    res = run_decode(t, K)
+    check_decode(d, res, where="2M decode")
+    for a, b in zip(res, run_decode(t, K, flags=mqa.FLAG_NO_PREFILTER)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert mqa.mqa_fp4_status() == 0
+
+
 def test_infinite_and_nan_weights_order_exactly_like_the_oracle():
     """Rows whose scores hold +-inf and NaN (a weight of +-inf gives +-inf where
     the head's dot is positive and NaN where it is 0; a NaN weight makes every
