@@ -129,8 +129,9 @@ def test_random_case(seed):
 
 @pytest.mark.parametrize("seed", range(N_LONG_CASES))
 def test_random_long_case(seed):
-    """One context split against several (calibration split too), every row
-    against the oracle, and the decode form bit-equal to both."""
+    """One context split against several (calibration split too) and against
+    the automatic count, every row against the oracle, and the decode form
+    bit-equal to them."""
     if not gu.has_gpu():
         pytest.skip("no GPU")
     inp, splits = draw_long_case(seed)
@@ -139,9 +140,10 @@ def test_random_long_case(seed):
     print(tag, flush=True)
     base = gu.run_fused(dev, inp.K, flags=1)
     check_rows(inp, range(inp.Q), *base, where=f"{tag} one split")
-    got = gu.run_fused(dev, inp.K, flags=splits)
-    for a, b in zip(base, got):
-        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag}: splits change the outputs"
+    for f in (splits, 0):   # the drawn count, then the automatic one
+        got = gu.run_fused(dev, inp.K, flags=f)
+        for a, b in zip(base, got):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{tag}: splits {f} change the outputs"
     dec = run_decode_one_sequence(dev, inp.K)
     for i, what in enumerate(("raw", "slot", "count", "score")):
         assert np.array_equal(np.asarray(base[i]).view(np.uint32), np.asarray(dec[i]).view(np.uint32)), \
