@@ -941,8 +941,10 @@ void launch_decode_k(const DecArgs& a0, const PathArgs& p, int mode, int cus, in
   int occ = per_cu.load(std::memory_order_relaxed);
   if (occ == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, decode_gscan_kernel<K>, kDecThreads, 0) != hipSuccess ||
-        occ < 1)
+        occ < 1) {
+      (void)hipGetLastError();   // a failed query is not the launch's error
       occ = kDecScanBlocksPerCu;
+    }
     per_cu.store(occ, std::memory_order_relaxed);
   }
   const int64_t blocks = min(static_cast<int64_t>(occ) * cus, static_cast<int64_t>(kDecScanWaves / kDecWaves));

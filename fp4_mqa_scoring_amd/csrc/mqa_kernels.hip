@@ -1490,8 +1490,11 @@ static hipError_t launch_gated_k(const PathArgs& p, const GatedScratch& g, int32
       static std::atomic<int> per_cu{0};
       int occ = per_cu.load(std::memory_order_relaxed);
       if (occ == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_kernel<K>, kCtaThreads, 0) != hipSuccess || occ < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, scan_kernel<K>, kCtaThreads, 0) != hipSuccess ||
+            occ < 1) {
+          (void)hipGetLastError();   // a failed query is not the launch's error
           occ = 2;
+        }
         per_cu.store(occ, std::memory_order_relaxed);
       }
       const int64_t items = static_cast<int64_t>(tiles) * splits, resident = static_cast<int64_t>(occ) * cus;
