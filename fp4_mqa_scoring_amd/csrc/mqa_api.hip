@@ -37,7 +37,10 @@ int32_t device_info(int dev, DeviceInfo* out) {
   DeviceInfo& d = g_dev[dev];
   if (!d.probed) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MQA_ERR_HIP;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MQA_ERR_HIP;
+    }
     d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
     d.cus = prop.multiProcessorCount;
     d.probed = true;
@@ -74,8 +77,9 @@ struct DeviceGuard {
 };
 
 int32_t stream_device(hipStream_t st, int* dev) {
-  if (st == nullptr) return hipGetDevice(dev) == hipSuccess ? MQA_OK : MQA_ERR_HIP;
-  return hipStreamGetDevice(st, dev) == hipSuccess ? MQA_OK : MQA_ERR_DEVICE;
+  const bool ok = (st == nullptr ? hipGetDevice(dev) : hipStreamGetDevice(st, dev)) == hipSuccess;
+  if (!ok) (void)hipGetLastError();   // reported through the return code only
+  return ok ? MQA_OK : st == nullptr ? MQA_ERR_HIP : MQA_ERR_DEVICE;
 }
 
 // A non-null pointer must be device (or managed) memory of device `dev`.
