@@ -64,9 +64,15 @@ struct DeviceGuard {
   int saved = -1;
   bool changed = false;
   int32_t enter(int dev) {
-    if (hipGetDevice(&saved) != hipSuccess) return MQA_ERR_HIP;
+    if (hipGetDevice(&saved) != hipSuccess) {
+      (void)hipGetLastError();
+      return MQA_ERR_HIP;
+    }
     if (saved != dev) {
-      if (hipSetDevice(dev) != hipSuccess) return MQA_ERR_HIP;
+      if (hipSetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MQA_ERR_HIP;
+      }
       changed = true;
     }
     return MQA_OK;

@@ -56,6 +56,13 @@
  * refused with MQA_ERR_CAPTURING (PR 5282, Scope: no graph capture in the first
  * version). Calls on the same stream are ordered; calls on different streams
  * use separate stream-ordered scratch and may run concurrently.
+ *
+ * Scratch of the allocating entry points comes from the device's default
+ * memory pool (hipMallocAsync on `stream`, hipFreeAsync when the call's work
+ * is enqueued). On its first call on a device the library sets that pool's
+ * release threshold to its maximum, so that freed scratch stays in the pool
+ * for the next call instead of going back to the driver: a process-wide
+ * setting of the default pool, which other users of that pool share.
  */
 #ifndef MQA_FP4_TOPK_H
 #define MQA_FP4_TOPK_H
