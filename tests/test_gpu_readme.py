@@ -38,3 +38,31 @@ def test_readme_example():
                                    d_cnt)
     torch.cuda.synchronize()
     assert np.array_equal(d_raw.cpu().numpy(), raw) and np.array_equal(d_slot.cpu().numpy(), slot)
+
+
+def test_readme_decode_example():
+    """The README's decode example runs as written; the graph replay's outputs
+    equal an eager call's, and every row matches the oracle through its
+    sequence's block table."""
+    if not gu.has_gpu():
+        pytest.skip("no GPU")
+    import torch
+    text = open(os.path.join(ROOT, "README.md")).read()
+    code = re.findall(r"```python\n(.*?)```", text, re.S)[1]
+    ns = {}
+    exec(compile(code, "README.md", "exec"), ns)
+    torch.cuda.synchronize()
+    cpu = lambda n: ns[n].cpu().numpy()
+    replayed = [cpu(n) for n in ("raw", "slot", "count")]
+    ns["step"]()
+    torch.cuda.synchronize()
+    for a, n in zip(replayed, ("raw", "slot", "count")):
+        assert np.array_equal(a, cpu(n)), n
+    K = ns["K"]
+    d = synth.DecodeInputs(cpu("q"), cpu("q_scale"), cpu("k_pages"), cpu("k_scale"), cpu("weights"),
+                           cpu("block_table"), cpu("seq_of_row"), cpu("row_start"), cpu("row_end"),
+                           ns["lens"].numpy().astype(np.int64), K, name="README decode example")
+    raw, slot, count = replayed
+    assert np.all(count == K)
+    for r in range(d.Q):
+        check_rows(d.view(int(d.seq_of_row[r])), [r], raw, slot, count, where=f"README decode row {r}")
