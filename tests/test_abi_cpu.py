@@ -217,3 +217,37 @@ def test_allocation_free_entry_point_checks_its_limit_on_host(lib):
     assert call(2045, 512) != -4
     assert call(10, 700) == -1
     assert call(10, 512, flags=0x500) == -8
+
+
+def test_binding_rejects_malformed_tensors_before_the_library():
+    """The Python binding only marshals pointers, so it refuses any tensor whose
+    dtype, contiguity or shape differs from the header's layout (host tensors:
+    nothing reaches the library)."""
+    import torch
+    import fp4_mqa_scoring_amd as mqa
+    Q, P, K = 4, 8, 512
+
+    def args(**over):
+        a = dict(q=torch.zeros(Q, 64, 64, dtype=torch.uint8), q_scale=torch.zeros(Q, 64, 4, dtype=torch.uint8),
+                 k_pages=torch.zeros(P, 64, 64, dtype=torch.uint8), k_scale=torch.zeros(P, 64, 4, dtype=torch.uint8),
+                 weights=torch.zeros(Q, 64), page_table=torch.zeros(P, dtype=torch.int32),
+                 row_start=torch.zeros(Q, dtype=torch.int32), row_end=torch.zeros(Q, dtype=torch.int32), K=K,
+                 out_raw=torch.zeros(Q, K, dtype=torch.int32), out_slot=torch.zeros(Q, K, dtype=torch.int32),
+                 out_count=torch.zeros(Q, dtype=torch.int32))
+        a.update(over)
+        return a
+
+    bad = [
+        (TypeError, dict(weights=torch.zeros(Q, 64, dtype=torch.float16))),               # dtype
+        (TypeError, dict(q="not a tensor")),
+        (ValueError, dict(q=torch.zeros(Q, 64, 128, dtype=torch.uint8)[:, :, ::2])),     # strided view
+        (ValueError, dict(weights=torch.zeros(64, Q).t())),                              # transposed
+        (ValueError, dict(q_scale=torch.zeros(Q, 64, 2, dtype=torch.uint8))),             # shape
+        (ValueError, dict(k_scale=torch.zeros(P + 1, 64, 4, dtype=torch.uint8))),
+        (ValueError, dict(row_end=torch.zeros(Q + 1, dtype=torch.int32))),
+        (ValueError, dict(out_raw=torch.zeros(Q, K + 1, dtype=torch.int32))),
+        (ValueError, dict(out_count=torch.zeros(Q - 1, dtype=torch.int32))),
+    ]
+    for exc, over in bad:
+        with pytest.raises(exc):
+            mqa.mqa_fp4_topk_prefill(**args(**over))
